@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LM-head + cross-entropy loss, forward + backward, on one MI355X.
+
+One step = lmce_fwd (loss, per-row lse) + lmce_bwd_dh + lmce_bwd_dW (together
+exactly lmce_bwd) over the whole workload, inputs already resident in HBM.
+Default workload: the Qwen3-8B head at one GPU's share of a 1,048,576-token
+sequence (L = 131072, H = 4096, V = 151936, Zipf(1.1) labels, row 0 ignored),
+synthetic and seeded.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value            tokens/s of the whole step (L * steps / wall time)
+  config           workload sizes, chunk_rows, per-call times, achieved TFLOP/s and
+                   fraction of the bf16 dense MFMA peak for the whole step
+  roofline         the dominant call (timed with HIP events on the stream it is
+                   launched on): algorithmic flops per launch / its mean duration
+  cpu_baseline     the fp64 CPU oracle timed on a bounded sample of the workload
+
+Flop accounting (algorithmic, independent of the schedule):
+  forward      2 L H V            (logits of every row; lse is returned for all)
+  backward     6 N H V            (logit recompute, dh = G W, dW = G^T h; N valid rows)
+  lmce_bwd_dh  3 N H V            (half of the recompute + the dh contraction)
+  lmce_bwd_dW  3 N H V            (half of the recompute + the dW contraction)
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused LM-head+CE fwd+bwd tokens/s and % bf16 MFMA peak at Qwen3-8B L=131072"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, W_cpu, h_rows, y_rows):
+    """fp64 oracle on the first rows of the workload at full H and V."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+
+    h_np = h_rows.float().numpy()
+    y_np = y_rows.numpy()
+    W_np = W_cpu.float().numpy()
+    oracle.forward(h_np[:8], W_np, y_np[:8])  # warm BLAS
+    t0 = time.perf_counter()
+    oracle.fwd_bwd(h_np, W_np, y_np)
+    dt = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [os.cpu_count()])
+    n = h_np.shape[0]
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} rows of {wl.name} at full H={wl.H}, V={wl.V}: fp64 forward+backward in "
+                      f"{dt:.2f} s (full workload extrapolates to {wl.L / n * dt:.0f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3_8b_1m_shard")
+    ap.add_argument("--chunk-rows", type=int, default=None)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the loss on a single MI355X "
+              "(each GPU of a row-sharded job would run the same kernels on its own rows). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lm_head_chunked_amd as lm
+    from lm_head_chunked_amd import _lib, synth
+
+    _lib.load()
+    wl = synth.WORKLOADS[args.workload]
+    chunk = args.chunk_rows or wl.chunk_rows
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {wl.name} L={wl.L} H={wl.H} V={wl.V} chunk_rows={chunk}")
+
+    h, W, y = synth.make(wl, device=dev)
+    n_valid = int((y != -100).sum())
+    L, H, V = wl.L, wl.H, wl.V
+    ws_bytes = lm.lmce_workspace_size(L, H, V, chunk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(L, dtype=torch.float32, device=dev)
+    dh = torch.empty(L, H, dtype=torch.float32, device=dev)
+    dW = torch.empty(V, H, dtype=torch.float32, device=dev)
+    g = torch.ones((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    base_alloc = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        lm.lmce_fwd(h, W, y, -100, chunk, ws, loss, lse)
+        if ev is not None:
+            ev[1].record(stream)
+        lm.lmce_bwd_dh(h, W, y, lse, g, -100, chunk, ws, dh)
+        if ev is not None:
+            ev[2].record(stream)
+        lm.lmce_bwd_dW(h, W, y, lse, g, -100, chunk, ws, dW)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    if lm.lmce_read_status(ws) != _lib.LMCE_OK:
+        raise RuntimeError("label status error")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base_alloc
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dh_ms = [e[1].elapsed_time(e[2]) for e in events]
+    dW_ms = [e[2].elapsed_time(e[3]) for e in events]
+    ms_step = wall * 1000.0 / args.steps
+    log(f"[bench] {args.steps} steps: {ms_step:.1f} ms/step; fwd {statistics.mean(fwd_ms):.1f} ms, "
+        f"bwd_dh {statistics.mean(dh_ms):.1f} ms, bwd_dW {statistics.mean(dW_ms):.1f} ms; loss {float(loss):.5f}")
+
+    f_fwd = 2.0 * L * H * V
+    f_half_bwd = 3.0 * n_valid * H * V
+    f_alg = f_fwd + 2 * f_half_bwd
+    tflops = f_alg / (ms_step / 1000.0) / 1e12
+    calls = {
+        "lmce_fwd": (f_fwd, statistics.mean(fwd_ms)),
+        "lmce_bwd_dh": (f_half_bwd, statistics.mean(dh_ms)),
+        "lmce_bwd_dW": (f_half_bwd, statistics.mean(dW_ms)),
+    }
+    dom = max(calls, key=lambda k: calls[k][1])
+    dom_kernel = {"lmce_fwd": "k_fwd", "lmce_bwd_dh": "k_bwd_dh", "lmce_bwd_dW": "k_bwd_dW"}[dom]
+    dom_tflops = calls[dom][0] / (calls[dom][1] / 1000.0) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": L * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "L": L, "H": H, "V": V, "n_valid": n_valid, "chunk_rows": chunk,
+            "labels": wl.labels, "achieved_tflops": tflops, "peak_frac_bf16": tflops / PEAK_BF16_TFLOPS,
+            "fwd_ms": statistics.mean(fwd_ms), "bwd_dh_ms": statistics.mean(dh_ms),
+            "bwd_dW_ms": statistics.mean(dW_ms), "workspace_bytes": ws_bytes,
+            "peak_extra_alloc_bytes": int(peak_extra), "logits_fp32_bytes_avoided": L * V * 4,
+            "loss": float(loss), "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": dom_kernel, "call": dom, "achieved": dom_tflops,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None, "mean_ms": calls[dom][1],
+        },
+        "cpu_baseline": None,
+    }
+    del dh, dW, ws
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        W_cpu = W.cpu()
+        result["cpu_baseline"] = cpu_baseline(wl, W_cpu, h[: args.cpu_rows].cpu(), y[: args.cpu_rows].cpu())
+        log(f"[bench] cpu baseline {result['cpu_baseline']['value']:.1f} tokens/s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

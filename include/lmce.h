@@ -1,0 +1,142 @@
+/*
+ * lmce.h -- fused LM-head + cross-entropy (NLL) loss for AMD MI355X (gfx950).
+ *
+ * The operation (TRL docs "Training Beyond 1M Tokens", section "The loss is
+ * the first thing to break"): the last hidden state h (L x H) is multiplied
+ * by the LM-head weight W (V x H) to give logits z = h W^T (L x V), and the
+ * loss is the cross entropy of z against the target labels.  Section "The
+ * massive logits matrix: chunk it" of the same page computes it a block of
+ * rows at a time so that the L x V logits are never held whole; rows split
+ * cleanly because each row's softmax runs over its own vocabulary only.
+ *
+ * This library goes further than row chunks: no logits block is ever written
+ * to memory.  Each logit tile exists only in registers while a kernel folds
+ * it into a running per-row log-sum-exp (forward) or into the gradient
+ * contractions (backward).
+ *
+ *   lse_i  = log sum_v exp(z_iv)                       every row i
+ *   loss   = sum_{i : y_i != ignore_index} (lse_i - z_{i,y_i}) / N
+ *   G_iv   = g / N * [y_i != ignore_index] * (softmax(z_i)_v - [v == y_i])
+ *   dh     = G W        (L x H)
+ *   dW     = G^T h      (V x H)
+ *
+ * N is the number of rows whose label is not ignore_index, g the upstream
+ * gradient of the scalar loss.  N == 0 gives loss = NaN and zero gradients.
+ *
+ * Conventions for every entry point:
+ *   - h and W are bf16, row-major and contiguous: h[i*H + k], W[v*H + k]
+ *     (W has the nn.Linear weight layout).  labels are int64 [L], already
+ *     shifted (labels[i] is the target of row i).  All outputs are fp32.
+ *   - Every pointer is a DEVICE pointer owned by the caller.  h, W, dh_out
+ *     and dW_out must be 16-byte aligned, labels 8-byte, workspace 256-byte,
+ *     the fp32 scalars and lse 4-byte; otherwise LMCE_ERR_NULL.
+ *     The library keeps no pointer after a call returns.
+ *   - Every call only enqueues work on `stream` and returns; it never
+ *     allocates device memory and never synchronises (except
+ *     lmce_read_status, which is documented as synchronising).
+ *   - The caller supplies a workspace of at least lmce_workspace_size()
+ *     bytes.  Calls that share a workspace must be ordered on one stream.
+ *   - Return value: LMCE_OK (0) or a negative lmce_status.  Argument errors
+ *     are detected before anything is enqueued.
+ *   - Limits: 1 <= L <= 2^24, 1 <= V <= 2^24, 64 <= H <= 16384 with
+ *     H % 64 == 0, chunk_rows a multiple of 32 in [32, 1024].
+ */
+#ifndef LMCE_H
+#define LMCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMCE_OK = 0,
+  LMCE_ERR_NULL = -1,        /* a required pointer is NULL or misaligned */
+  LMCE_ERR_SHAPE = -2,       /* L, H or V out of range */
+  LMCE_ERR_UNSUPPORTED = -3, /* H % 64 != 0, or chunk_rows not a multiple of 32 in [32, 1024] */
+  LMCE_ERR_WORKSPACE = -4,   /* workspace_bytes smaller than lmce_workspace_size() */
+  LMCE_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
+  LMCE_ERR_LABEL = -6        /* (asynchronous) a label is outside [0, V) and not ignore_index */
+} lmce_status;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int lmce_version(void);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* lmce_strerror(int status);
+
+/*
+ * Bytes of device workspace that lmce_fwd / lmce_bwd need for this shape.
+ * The size is O(L * segments + V * H-independent terms): it never holds an
+ * L x V array.  Writes the size to *bytes.  Returns LMCE_OK or a shape error.
+ */
+int lmce_workspace_size(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, size_t* bytes);
+
+/*
+ * Forward.  Page: TRL docs "Training Beyond 1M Tokens", sections "The loss is
+ * the first thing to break" (the definition) and "The massive logits matrix:
+ * chunk it" (row chunks of chunk_rows rows, 256 by default; the pieces are
+ * summed).
+ *
+ *   h        bf16 [L, H]   hidden states
+ *   W        bf16 [V, H]   LM-head weight
+ *   labels   int64 [L]     target of each row, or ignore_index
+ *   loss_out fp32 [1]      mean NLL over non-ignored rows (NaN if none, or if
+ *                          a label was out of range)
+ *   lse_out  fp32 [L]      log-sum-exp of every row's logits (ignored rows too)
+ *
+ * chunk_rows only shapes the schedule (rows whose vocabulary sweep is run as
+ * one unit); results do not depend on it.
+ * An out-of-range label is reported asynchronously: loss_out becomes NaN and
+ * lmce_read_status() returns LMCE_ERR_LABEL.
+ */
+int lmce_fwd(const void* h, const void* W, const int64_t* labels,
+             int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
+             float* loss_out, float* lse_out,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward.  Same page and sections; the gradient of the mean NLL is
+ * G = g/N * valid * (softmax - onehot).  Each logit tile is recomputed from
+ * h and W, turned into G in registers and contracted at once into
+ *   dh_out fp32 [L, H] = G W     (overwritten, not accumulated)
+ *   dW_out fp32 [V, H] = G^T h   (overwritten, not accumulated)
+ *
+ *   lse        fp32 [L]  the lse_out of lmce_fwd on the same inputs
+ *   grad_loss  fp32 [1]  device scalar g, the upstream gradient of the loss
+ * Other arguments as in lmce_fwd.  Ignored rows get exactly zero dh rows.
+ */
+int lmce_bwd(const void* h, const void* W, const int64_t* labels, const float* lse,
+             int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
+             const float* grad_loss, float* dh_out, float* dW_out,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of lmce_bwd, for callers that need only one gradient (a
+ * frozen LM head needs dh alone; a frozen trunk needs dW alone).  Same
+ * arguments and results as lmce_bwd for the gradient they produce; calling
+ * both equals one lmce_bwd.
+ */
+int lmce_bwd_dh(const void* h, const void* W, const int64_t* labels, const float* lse,
+                int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
+                const float* grad_loss, float* dh_out,
+                void* workspace, size_t workspace_bytes, void* stream);
+int lmce_bwd_dW(const void* h, const void* W, const int64_t* labels, const float* lse,
+                int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
+                const float* grad_loss, float* dW_out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Synchronises `stream` and returns the asynchronous status recorded in the
+ * workspace by the last lmce_fwd / lmce_bwd on it: LMCE_OK or LMCE_ERR_LABEL
+ * (or LMCE_ERR_HIP if the synchronisation itself failed).
+ */
+int lmce_read_status(const void* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMCE_H */

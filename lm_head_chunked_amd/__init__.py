@@ -1,1 +1,164 @@
-"""MI355X-native fused LM-head + cross-entropy (chunked NLL) loss."""
+"""MI355X-native fused LM-head + cross-entropy (chunked NLL) loss.
+
+Python binding of the C ABI in ``include/lmce.h``.  PyTorch only allocates
+device memory and supplies the current HIP stream; every step of the loss
+runs in the HIP kernels of ``liblmce.so``.  There is no CPU or PyTorch
+fallback: without the built library every call raises.
+
+Page: TRL docs "Training Beyond 1M Tokens", sections "The loss is the first
+thing to break" and "The massive logits matrix: chunk it" (256-row chunks by
+default).
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import LmceError
+
+IGNORE_INDEX = -100
+DEFAULT_CHUNK_ROWS = 256
+
+__all__ = [
+    "lmce_workspace_size",
+    "lmce_fwd",
+    "lmce_bwd",
+    "lmce_bwd_dh",
+    "lmce_bwd_dW",
+    "lmce_read_status",
+    "chunked_nll",
+    "LmceError",
+    "IGNORE_INDEX",
+    "DEFAULT_CHUNK_ROWS",
+]
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_inputs(h, W, labels):
+    if not (h.is_cuda and W.is_cuda and labels.is_cuda):
+        raise ValueError("h, W and labels must be device tensors")
+    if h.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise TypeError("h and W must be bfloat16")
+    if labels.dtype != torch.int64:
+        raise TypeError("labels must be int64")
+    if h.dim() != 2 or W.dim() != 2 or labels.dim() != 1:
+        raise ValueError("expected h [L, H], W [V, H], labels [L]")
+    if h.shape[1] != W.shape[1] or labels.shape[0] != h.shape[0]:
+        raise ValueError(f"shape mismatch: h {tuple(h.shape)}, W {tuple(W.shape)}, labels {tuple(labels.shape)}")
+    if not (h.is_contiguous() and W.is_contiguous() and labels.is_contiguous()):
+        raise ValueError("h, W and labels must be contiguous")
+    return h.shape[0], h.shape[1], W.shape[0]
+
+
+def lmce_workspace_size(L, H, V, chunk_rows=DEFAULT_CHUNK_ROWS) -> int:
+    """Bytes of device workspace lmce_fwd / lmce_bwd need (never an L x V buffer)."""
+    return _lib.workspace_size(L, H, V, chunk_rows)
+
+
+def _workspace(L, H, V, chunk_rows, device, workspace):
+    need = _lib.workspace_size(L, H, V, chunk_rows)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, needs {need}")
+    return workspace
+
+
+def lmce_fwd(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS, workspace=None,
+             loss_out=None, lse_out=None):
+    """Mean NLL loss (fp32 scalar tensor) and per-row logsumexp (fp32 [L])."""
+    L, H, V = _check_inputs(h, W, labels)
+    dev = h.device
+    ws = _workspace(L, H, V, chunk_rows, dev, workspace)
+    loss = torch.empty((), dtype=torch.float32, device=dev) if loss_out is None else loss_out
+    lse = torch.empty(L, dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    st = _lib.fwd(h.data_ptr(), W.data_ptr(), labels.data_ptr(), L, H, V, ignore_index, chunk_rows,
+                  loss.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(st, "lmce_fwd")
+    return loss, lse
+
+
+def lmce_bwd(h, W, labels, lse, grad_loss=None, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS,
+             workspace=None, dh_out=None, dW_out=None):
+    """dh (fp32 [L, H]) and dW (fp32 [V, H]) of grad_loss * loss (overwritten)."""
+    L, H, V = _check_inputs(h, W, labels)
+    dev = h.device
+    if lse.dtype != torch.float32 or lse.shape != (L,) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [L]")
+    if grad_loss is None:
+        grad_loss = torch.ones((), dtype=torch.float32, device=dev)
+    grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
+    ws = _workspace(L, H, V, chunk_rows, dev, workspace)
+    dh = torch.empty(L, H, dtype=torch.float32, device=dev) if dh_out is None else dh_out
+    dW = torch.empty(V, H, dtype=torch.float32, device=dev) if dW_out is None else dW_out
+    st = _lib.bwd(h.data_ptr(), W.data_ptr(), labels.data_ptr(), lse.data_ptr(), L, H, V, ignore_index, chunk_rows,
+                  grad_loss.data_ptr(), dh.data_ptr(), dW.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                  _stream(dev))
+    _lib.check(st, "lmce_bwd")
+    return dh, dW
+
+
+def _bwd_one(which, h, W, labels, lse, grad_loss, ignore_index, chunk_rows, workspace, out):
+    L, H, V = _check_inputs(h, W, labels)
+    dev = h.device
+    if lse.dtype != torch.float32 or lse.shape != (L,) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [L]")
+    if grad_loss is None:
+        grad_loss = torch.ones((), dtype=torch.float32, device=dev)
+    grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
+    ws = _workspace(L, H, V, chunk_rows, dev, workspace)
+    rows = L if which == "dh" else V
+    if out is None:
+        out = torch.empty(rows, H, dtype=torch.float32, device=dev)
+    fn = _lib.bwd_dh if which == "dh" else _lib.bwd_dW
+    st = fn(h.data_ptr(), W.data_ptr(), labels.data_ptr(), lse.data_ptr(), L, H, V, ignore_index, chunk_rows,
+            grad_loss.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(st, f"lmce_bwd_{which}")
+    return out
+
+
+def lmce_bwd_dh(h, W, labels, lse, grad_loss=None, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS,
+                workspace=None, dh_out=None):
+    """dh (fp32 [L, H]) alone, e.g. for a frozen LM head."""
+    return _bwd_one("dh", h, W, labels, lse, grad_loss, ignore_index, chunk_rows, workspace, dh_out)
+
+
+def lmce_bwd_dW(h, W, labels, lse, grad_loss=None, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS,
+                workspace=None, dW_out=None):
+    """dW (fp32 [V, H]) alone."""
+    return _bwd_one("dW", h, W, labels, lse, grad_loss, ignore_index, chunk_rows, workspace, dW_out)
+
+
+def lmce_read_status(workspace) -> int:
+    """Synchronises the current stream; LMCE_OK or LMCE_ERR_LABEL recorded by the last call."""
+    return _lib.read_status(workspace.data_ptr(), _stream(workspace.device))
+
+
+class _ChunkedNLL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, h, W, labels, ignore_index, chunk_rows):
+        L, H, V = _check_inputs(h, W, labels)
+        ws = _workspace(L, H, V, chunk_rows, h.device, None)
+        loss, lse = lmce_fwd(h, W, labels, ignore_index, chunk_rows, ws)
+        ctx.save_for_backward(h, W, labels, lse)
+        ctx.ignore_index = ignore_index
+        ctx.chunk_rows = chunk_rows
+        ctx.ws = ws
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        h, W, labels, lse = ctx.saved_tensors
+        dh, dW = lmce_bwd(h, W, labels, lse, grad_loss, ctx.ignore_index, ctx.chunk_rows, ctx.ws)
+        ctx.ws = None
+        return dh, dW, None, None, None
+
+
+def chunked_nll(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS):
+    """Differentiable mean NLL of log_softmax(h W^T) against labels (TRL's
+    ``loss_type="chunked_nll"``), computed without an L x V logits buffer."""
+    return _ChunkedNLL.apply(h, W, labels, ignore_index, chunk_rows)
