@@ -13,15 +13,16 @@
 namespace lmce {
 namespace {
 
-constexpr int64_t kMaxRows = int64_t(1) << 24;   // L and V limits (int32 grid math stays exact)
+constexpr int64_t kMaxRows = int64_t(1) << 21;   // L and V limits (32-bit buffer offsets stay exact)
 constexpr int64_t kMaxHidden = 16384;
+constexpr int kSpinLimit = 1 << 21;                // bound of every group wait (about a second)
 
 struct Plan {
   int64_t L, H, V;
-  int chunk_rows, tiles_per_chunk, n_chunks, segments, vtiles, vtiles_per_seg;
+  int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
   int64_t Lpad, Vpad;
-  int hs;
-  size_t off_zlabel, off_pm, off_ps, off_bsum, off_hT, off_WT, total;
+  int hs, group_size, xbuf_wgs;
+  size_t off_zlabel, off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -40,21 +41,23 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->H = H;
   p->V = V;
   p->chunk_rows = (int)chunk_rows;
-  p->tiles_per_chunk = (int)((chunk_rows + kTile - 1) / kTile);
+  // Forward row tiles: 256 tokens when chunks are whole multiples of 256,
+  // else 128.  Per-row arithmetic does not depend on the tile height.
+  p->tile_rows = (chunk_rows % 256 == 0) ? 256 : 128;
+  p->tiles_per_chunk = (int)((chunk_rows + p->tile_rows - 1) / p->tile_rows);
   p->n_chunks = (int)((L + chunk_rows - 1) / chunk_rows);
-  p->vtiles = (int)((V + kTile - 1) / kTile);
-  // Vocabulary segments: enough workgroups to fill the chip when L is small.
-  // Depends on L and V only, so that results never depend on chunk_rows.
-  const int64_t row_tiles = (L + kTile - 1) / kTile;
-  int64_t seg = (1024 + row_tiles - 1) / row_tiles;
-  int64_t seg_cap = p->vtiles / 4 > 0 ? p->vtiles / 4 : 1;
-  if (seg > seg_cap) seg = seg_cap;
-  if (seg < 1) seg = 1;
-  p->vtiles_per_seg = (int)((p->vtiles + seg - 1) / seg);
+  p->ntiles = p->n_chunks * p->tiles_per_chunk;
+  p->vtiles = (int)((V + kVTile - 1) / kVTile);
+  // Vocabulary segments: a function of V only, so that results never depend
+  // on chunk_rows.  Eight segments (one per XCD position) when V allows.
+  int seg = p->vtiles >= 32 ? 8 : (p->vtiles / 4 > 0 ? p->vtiles / 4 : 1);
+  p->vtiles_per_seg = (p->vtiles + seg - 1) / seg;
   p->segments = (p->vtiles + p->vtiles_per_seg - 1) / p->vtiles_per_seg;
-  p->Lpad = (L + kTile - 1) / kTile * kTile;
-  p->Vpad = (V + kTile - 1) / kTile * kTile;
-  p->hs = (H % 256 == 0) ? 256 : (H % 128 == 0) ? 128 : 64;
+  p->xcd_map = (p->segments == 8 && p->ntiles % 32 == 0) ? 1 : 0;
+  p->Lpad = (L + 127) / 128 * 128;
+  p->Vpad = (V + 127) / 128 * 128;
+  p->hs = (H % 128 == 0) ? 128 : 64;
+  p->group_size = (int)(H / p->hs);
 
   size_t off = align256(sizeof(WsHeader));
   p->off_zlabel = off;
@@ -64,11 +67,21 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->off_ps = off;
   off = align256(off + sizeof(float) * (size_t)L * (size_t)p->segments);
   p->off_bsum = off;
-  off = align256(off + sizeof(float) * (size_t)((L + 255) / 256));
+  off = align256(off + sizeof(float) * (size_t)((L + 63) / 64));
   p->off_hT = off;
   off = align256(off + sizeof(uint16_t) * (size_t)H * (size_t)p->Lpad);
   p->off_WT = off;
   off = align256(off + sizeof(uint16_t) * (size_t)H * (size_t)p->Vpad);
+  p->off_sync = off;
+  off = align256(off + sizeof(unsigned) * (size_t)kMaxBwdWGs * kSyncStride);
+  p->off_xbuf = off;
+  // Exchange slots for as many backward workgroups as can be useful (at most
+  // one group per row block or vocabulary block, at most kMaxBwdWGs).
+  const int64_t items = (L + 255) / 256 > (V + 255) / 256 ? (L + 255) / 256 : (V + 255) / 256;
+  int64_t wgs = items * p->group_size;
+  if (wgs > kMaxBwdWGs) wgs = kMaxBwdWGs;
+  p->xbuf_wgs = (int)wgs;
+  off = align256(off + (size_t)wgs * kXbufPerWG);
   p->total = off;
   return LMCE_OK;
 }
@@ -132,11 +145,13 @@ extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int
   a.V = V;
   a.ignore_index = ignore_index;
   a.chunk_rows = p.chunk_rows;
+  a.tile_rows = p.tile_rows;
   a.tiles_per_chunk = p.tiles_per_chunk;
-  a.n_chunks = p.n_chunks;
+  a.ntiles = p.ntiles;
   a.segments = p.segments;
   a.vtiles = p.vtiles;
   a.vtiles_per_seg = p.vtiles_per_seg;
+  a.xcd_map = p.xcd_map;
   a.hdr = hdr;
   a.zlabel = at<float>(workspace, p.off_zlabel);
   a.part_m = at<float>(workspace, p.off_pm);
@@ -181,12 +196,27 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
   a.ignore_index = ignore_index;
   a.Lpad = p.Lpad;
   a.Vpad = p.Vpad;
-  a.vtiles = p.vtiles;
+  a.group_size = p.group_size;
+  a.spin_limit = kSpinLimit;
+  a.sync = at<unsigned>(workspace, p.off_sync);
+  a.xbuf = at<uint16_t>(workspace, p.off_xbuf);
   a.hdr = hdr;
   a.dh = dh_out;
   a.dW = dW_out;
-  if ((which & 1) && launch_bwd_dh(a, p.hs, s) != hipSuccess) return LMCE_ERR_HIP;
-  if ((which & 2) && launch_bwd_dW(a, p.hs, s) != hipSuccess) return LMCE_ERR_HIP;
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool dh = pass == 0;
+    if (!(which & (dh ? 1 : 2))) continue;
+    int resident = 0;
+    if (bwd_resident_wgs(dh, p.hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
+    if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
+    const int64_t items = dh ? (L + 255) / 256 : (V + 255) / 256;  // row blocks or vocabulary blocks
+    int64_t groups = resident / p.group_size;
+    if (groups > items) groups = items;
+    if (groups < 1) return LMCE_ERR_UNSUPPORTED;
+    a.n_groups = (int)groups;
+    if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
+    if (launch_bwd_group(dh, a, p.hs, (int)groups * p.group_size, s) != hipSuccess) return LMCE_ERR_HIP;
+  }
   return LMCE_OK;
 }
 
@@ -218,5 +248,7 @@ extern "C" int lmce_read_status(const void* workspace, void* stream) {
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return LMCE_ERR_HIP;
   WsHeader hdr;
   if (hipMemcpy(&hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost) != hipSuccess) return LMCE_ERR_HIP;
-  return hdr.status == 0 ? LMCE_OK : LMCE_ERR_LABEL;
+  if (hdr.status & kStatusLabel) return LMCE_ERR_LABEL;
+  if (hdr.status & kStatusSync) return LMCE_ERR_HIP;
+  return LMCE_OK;
 }

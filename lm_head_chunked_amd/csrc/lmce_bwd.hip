@@ -1,0 +1,342 @@
+// Backward kernels of the fused LM-head + cross-entropy loss (gfx950).
+//
+// Page: TRL docs "Training Beyond 1M Tokens", section "The massive logits
+// matrix: chunk it" (per-row pieces); the gradient of the mean NLL is
+// G = g/N * valid * (softmax - onehot), dh = G W and dW = G^T h.
+//
+// dh and dW are H wide: a 256 x H fp32 accumulator (4 MiB at H = 4096) does
+// not fit in one compute unit, so each pass runs as groups of s = H / HS
+// workgroups, workgroup j of a group owning an HS-wide slice of the
+// accumulator in registers.  In every round each member recomputes ONE
+// full-H logit tile with MFMA, turns it into bf16 G in registers and writes it
+// to the group's exchange slot; after a group barrier every member
+// contracts all s tiles of the round into its own slice.  Each logit is thus
+// recomputed exactly once per pass and no logit or G tile ever exists for
+// more than one round (the exchange holds 2 x s tiles per group).
+//
+//   k_bwd_dh : group = 256 rows of h; rounds sweep the vocabulary, 128 per
+//              member; dh[rows][slice] += G W   (row-owned, no atomics)
+//   k_bwd_dW : group = 256 vocabulary rows; rounds sweep the tokens, 128 per
+//              member; dW[rows][slice] += G^T h (vocabulary-owned, no atomics)
+//
+// The groups run as one cooperative launch (all workgroups resident).  The
+// exchange uses device-coherent (sc1) stores and loads and a per-group
+// arrival counter; every wait is bounded and reports a sync error instead of
+// hanging.
+
+#include "lmce_device.h"
+#include "lmce_internal.h"
+
+namespace lmce {
+
+// out[c][r] = in[r][c] for r < R, 0 for R <= r < Rpad.  in is [R x C]
+// row-major, out is [C x Rpad].  64x64 tiles through LDS; C % 64 == 0.
+__global__ __launch_bounds__(256) void k_transpose(const u16* __restrict__ in, int64_t R, int64_t C,
+                                                   u16* __restrict__ out, int64_t Rpad) {
+  __shared__ u16 t[64][66];
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i >> 6, cc = i & 63;
+    const int64_t r = r0 + rr;
+    t[rr][cc] = (r < R) ? in[r * C + c0 + cc] : (u16)0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i >> 6, rr = i & 63;
+    out[(c0 + cc) * Rpad + r0 + rr] = t[rr][cc];
+  }
+}
+
+__global__ void k_zero_u32(unsigned* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Position of workgroup b in XCD-major order (workgroups are dispatched to
+// the 8 XCDs round-robin), so that the members of a group share an L2.
+__device__ __forceinline__ int xcd_major(int b, int nwg) {
+  if (nwg % 8 != 0) return b;
+  return (b & 7) * (nwg >> 3) + (b >> 3);
+}
+
+// All s members of group g have written round `epoch`; bounded wait.
+// Returns false (and records kStatusSync) if the group did not arrive.
+__device__ __forceinline__ bool group_arrive_wait(unsigned* ctr, unsigned target, int spin_limit, WsHeader* hdr,
+                                                  int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's exchange stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int n = 0, ok = 1;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++n > spin_limit) {
+        ok = 0;
+        break;
+      }
+    }
+    if (!ok) __hip_atomic_fetch_or(&hdr->status, kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = ok;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// ---------------------------------------------------------------- dh pass
+// Group = 256 rows.  Round k: member j recomputes the logit tile of
+// vocabulary rows [(k*s + j)*128, +128) against the group's rows (A = W,
+// B = h, so the tile is z^T: vocabulary on M, tokens on N), forms
+// G[token][v] and stores it into columns [j*128, +128) of the round's slot
+// [256 tokens][s*128].  Then every member accumulates
+//   dh[rows][c0 .. c0+HS] += slot[256][K] * W^T[c0 .. c0+HS][round's vocabulary]
+// with K = 128 * (tiles in the round).
+template <int HS>
+__global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
+  using P = TileGemm<128, 256, 0>;       // producer: 128 vocabulary x 256 tokens
+  using C = TileGemm<256, HS, kAuxSc1>;  // consumer: 256 tokens x HS columns
+  constexpr int LDS = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ int s_flag;
+
+  const int s = p.group_size;
+  const int q = xcd_major(blockIdx.x, gridDim.x);
+  const int g = q / s, j = q % s;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t H = p.H, V = p.V, L = p.L;
+  const int64_t c0 = (int64_t)j * HS;
+  const int64_t ldx = (int64_t)s * 128;  // slot row length (elements)
+  // per-lane part of an exchange store: row lane%32, 4 columns per lane half
+  const uint32_t xvoff = (uint32_t)(((lane & 31) * ldx + ((lane >> 5) << 2)) * 2);
+  const int vt128 = (int)((V + 127) / 128);
+  const int rounds = (vt128 + s - 1) / s;
+  const int nrb = (int)((L + 255) / 256);
+  const int n_valid = p.hdr->n_valid;
+  const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
+  unsigned epoch = 0;
+
+  for (int rb = g; rb < nrb; rb += p.n_groups) {
+    const int64_t r0 = (int64_t)rb * 256;
+    const int64_t rend = min(r0 + 256, L);
+    // producer wave (wm: vocabulary half, wn: token half); lane's 4 tokens
+    float lse2[4], scale[4];
+    int64_t lab[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int64_t t = r0 + wn * 128 + nb * 32 + (lane & 31);
+      const int64_t y = t < rend ? p.labels[t] : p.ignore_index;
+      const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
+      lab[nb] = valid ? y : INT64_MIN / 2;
+      scale[nb] = valid ? gscale : 0.f;
+      lse2[nb] = t < rend ? p.lse[t] * kLog2e : INFINITY;  // rows past L: probability 0
+    }
+    const rsrc_t rh = make_rsrc(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2);
+
+    f32x16 dacc[C::MB][C::NB];
+    zero_acc(dacc);
+    for (int k = 0; k < rounds; ++k, ++epoch) {
+      u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * 256 * ldx;
+      const rsrc_t rslot = make_rsrc(slot, (uint64_t)256 * ldx * 2);
+      const int vt = k * s + j;
+      if (vt < vt128) {
+        const int64_t v0 = (int64_t)vt * 128;
+        f32x16 z[P::MB][P::NB];
+        zero_acc(z);
+        P::run(make_rsrc(p.W + v0 * H, (uint64_t)(V - v0) * H * 2), (uint32_t)(H * 2), 0, rh, (uint32_t)(H * 2), 0,
+               (int)H, lds, z);
+        // G[token][v] = scale * (exp(z - lse) - [v == y]); 4 consecutive v per store.
+        // Tile-local 32-bit coordinates: vl = v - v0, label at lab - v0.
+        const int vlim = (int)min<int64_t>(V - v0, 128);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int tl = wn * 128 + nb * 32 + (lane & 31);
+          const int64_t dl = lab[nb] - v0;
+          const int yl = (dl >= 0 && dl < 128) ? (int)dl : -1;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              float gv[4];
+              const int vl0 = wm * 64 + mb * 32 + acc_row(qq * 4, lane);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float pr = exp2_fast(__builtin_fmaf(z[mb][nb][qq * 4 + e], kLog2e, -lse2[nb]));
+                pr = (vl0 + e == yl) ? pr - 1.f : pr;
+                gv[e] = pr * ((vl0 + e < vlim) ? scale[nb] : 0.f);
+              }
+              const uint32_t soff = (uint32_t)(((wn * 128 + nb * 32) * ldx + j * 128 + wm * 64 + mb * 32 + qq * 8) * 2);
+              store_sc1_b64(rslot, xvoff, soff, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
+        return;
+      const int ntl = min(s, vt128 - k * s);
+      const int64_t vbase = (int64_t)k * s * 128;
+      C::run(make_rsrc(slot, (uint64_t)256 * ldx * 2), (uint32_t)(ldx * 2), 0,
+             make_rsrc(p.WT + c0 * p.Vpad + vbase, (uint64_t)HS * p.Vpad * 2), (uint32_t)(p.Vpad * 2), 0, ntl * 128,
+             lds, dacc);
+    }
+    // dh[r][c] for r < L (waves: wm token half, wn column half)
+    store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 128, wn * (HS / 2), lane);
+  }
+}
+
+// ---------------------------------------------------------------- dW pass
+// Group = 256 vocabulary rows.  Round k: member j recomputes the logit tile
+// of tokens [(k*s + j)*128, +128) against the group's vocabulary rows (A = h,
+// B = W: tokens on M, vocabulary on N), forms G^T[v][token] and stores it
+// into columns [j*128, +128) of the round's slot [256 v][s*128].  Then
+//   dW[v rows][c0 .. c0+HS] += slot[256][K] * h^T[c0 .. c0+HS][round's tokens].
+template <int HS>
+__global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
+  using P = TileGemm<128, 256, 0>;       // producer: 128 tokens x 256 vocabulary
+  using C = TileGemm<256, HS, kAuxSc1>;  // consumer: 256 vocabulary x HS columns
+  constexpr int LDS = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  __shared__ float row_lse2[128], row_scale[128];
+  __shared__ int row_lab[128];  // label - v0 of the group's vocabulary block, or -1
+  __shared__ int s_flag;
+
+  const int s = p.group_size;
+  const int q = xcd_major(blockIdx.x, gridDim.x);
+  const int g = q / s, j = q % s;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t H = p.H, V = p.V, L = p.L;
+  const int64_t c0 = (int64_t)j * HS;
+  const int64_t ldx = (int64_t)s * 128;
+  const uint32_t xvoff = (uint32_t)(((lane & 31) * ldx + ((lane >> 5) << 2)) * 2);
+  const int rt128 = (int)((L + 127) / 128);
+  const int rounds = (rt128 + s - 1) / s;
+  const int nvb = (int)((V + 255) / 256);
+  const int n_valid = p.hdr->n_valid;
+  const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
+  unsigned epoch = 0;
+
+  for (int vb = g; vb < nvb; vb += p.n_groups) {
+    const int64_t v0 = (int64_t)vb * 256;
+    const rsrc_t rw = make_rsrc(p.W + v0 * H, (uint64_t)(V - v0) * H * 2);
+    f32x16 dacc[C::MB][C::NB];
+    zero_acc(dacc);
+    for (int k = 0; k < rounds; ++k, ++epoch) {
+      u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * 256 * ldx;
+      const rsrc_t rslot = make_rsrc(slot, (uint64_t)256 * ldx * 2);
+      const int rt = k * s + j;
+      if (rt < rt128) {
+        const int64_t r0 = (int64_t)rt * 128;
+        const int64_t rend = min(r0 + 128, L);
+        if (threadIdx.x < 128) {
+          const int64_t t = r0 + threadIdx.x;
+          const int64_t y = t < rend ? p.labels[t] : p.ignore_index;
+          const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
+          row_lab[threadIdx.x] = (valid && y >= v0 && y < v0 + 256) ? (int)(y - v0) : -1;
+          row_scale[threadIdx.x] = valid ? gscale : 0.f;
+          row_lse2[threadIdx.x] = t < rend ? p.lse[t] * kLog2e : INFINITY;
+        }
+        f32x16 z[P::MB][P::NB];
+        zero_acc(z);
+        // (the GEMM's first barrier orders the row_* writes before their use)
+        P::run(make_rsrc(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2), (uint32_t)(H * 2), 0, rw, (uint32_t)(H * 2),
+               0, (int)H, lds, z);
+        // G^T[v][token]: lane = v (column), 4 consecutive tokens per store.
+        // Token data is read once per 4-token group and reused for the
+        // lane's 4 vocabulary columns; columns past V get a zero factor.
+        const int vlim = (int)min<int64_t>(V - v0, 256);
+        float vmask[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) vmask[nb] = (wn * 128 + nb * 32 + (lane & 31) < vlim) ? 1.f : 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int tl0 = wm * 64 + mb * 32 + acc_row(qq * 4, lane);
+            float tlse[4], tsc[4];
+            int tlab[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              tlse[e] = row_lse2[tl0 + e];
+              tsc[e] = row_scale[tl0 + e];
+              tlab[e] = row_lab[tl0 + e];
+            }
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const int vl = wn * 128 + nb * 32 + (lane & 31);
+              float gv[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float pr = exp2_fast(__builtin_fmaf(z[mb][nb][qq * 4 + e], kLog2e, -tlse[e]));
+                pr = (vl == tlab[e]) ? pr - 1.f : pr;
+                gv[e] = pr * (tsc[e] * vmask[nb]);
+              }
+              const uint32_t soff = (uint32_t)(((wn * 128 + nb * 32) * ldx + j * 128 + wm * 64 + mb * 32 + qq * 8) * 2);
+              store_sc1_b64(rslot, xvoff, soff, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+      if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
+        return;
+      const int ntl = min(s, rt128 - k * s);
+      const int64_t rbase = (int64_t)k * s * 128;
+      C::run(make_rsrc(slot, (uint64_t)256 * ldx * 2), (uint32_t)(ldx * 2), 0,
+             make_rsrc(p.hT + c0 * p.Lpad + rbase, (uint64_t)HS * p.Lpad * 2), (uint32_t)(p.Lpad * 2), 0, ntl * 128,
+             lds, dacc);
+    }
+    store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, dacc, wm * 128, wn * (HS / 2), lane);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st) {
+  dim3 grid((unsigned)(Rpad / 64), (unsigned)(C / 64));
+  hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, st, (const u16*)in, R, C, (u16*)out, Rpad);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+namespace {
+
+template <int HS>
+const void* pick_kernel(bool dh) {
+  return dh ? reinterpret_cast<const void*>(&k_bwd_dh<HS>) : reinterpret_cast<const void*>(&k_bwd_dW<HS>);
+}
+
+const void* bwd_kernel(bool dh, int hs) {
+  if (hs == 128) return pick_kernel<128>(dh);
+  return pick_kernel<64>(dh);
+}
+
+}  // namespace
+
+hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs) {
+  int dev = 0, cus = 0, per = 0, coop = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+  if (e != hipSuccess) return e;
+  if (!coop) return hipErrorNotSupported;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_kernel(dh, hs), kThreads, 0);
+  if (e != hipSuccess) return e;
+  *wgs = cus * per;
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int hs, int n_wgs, hipStream_t st) {
+  BwdArgs copy = a;
+  void* args[] = {&copy};
+  return hipLaunchCooperativeKernel(bwd_kernel(dh, hs), dim3((unsigned)n_wgs), dim3(kThreads), args, 0, st);
+}
+
+}  // namespace lmce

@@ -1,0 +1,231 @@
+// Device-side building blocks for gfx950 (CDNA4): vector types, the bf16
+// MFMA, buffer resources, the swizzled LDS stage layout and the pipelined
+// MFMA tile GEMM shared by every kernel of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmce {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+#define LMCE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int kThreads = 256;                    // 4 waves of 64 lanes
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;              // running max before any value
+constexpr int kAuxSc1 = 16;                      // cache policy: coherent at device scope
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void zero(f32x16& x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = 0.f;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The wave index within the workgroup, known to the compiler as uniform
+// (scalar register), so that addresses built from it stay scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// The lane index, hidden from loop-invariant code motion: addresses derived
+// from it are recomputed where they are used instead of being hoisted out of
+// the long loops and kept live in registers.
+__device__ __forceinline__ int lane_id() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+// v_mfma_f32_32x32x16 result layout: lane l holds column l % 32 of the
+// 32x32 block; its register r holds this row.
+__device__ __forceinline__ int acc_row(int reg, int lane) { return ((reg >> 2) << 3) + ((lane >> 5) << 2) + (reg & 3); }
+
+// (m, s) <- merge of two partial log-sum-exp states (s relative to m).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  s = s * exp2_fast((m - M) * kLog2e) + s2 * exp2_fast((m2 - M) * kLog2e);
+  m = M;
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return 0,
+// stores past the end are dropped.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const int n = bytes > 0x7ffff000ull ? 0x7ffff000 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Barrier across the workgroup without the memory fence of __syncthreads():
+// outstanding LDS-DMA loads of the pipeline stay in flight.
+__device__ __forceinline__ void raw_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ------------------------------------------------------------------ stages
+// A pipeline stage holds ROWS rows x 32 bf16 (64 bytes = four 16-byte chunks
+// per row).  Logical chunk c of row r sits in physical slot c ^ swz(r), which
+// spreads the eight (32-bank) or sixteen (64-bank) rows read together by a
+// ds_read_b128 over distinct banks.
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
+
+// One wave-level LDS-DMA load moves 1 KiB: lane i lands at lds_base + 16*i,
+// i.e. rows r0 .. r0+15, physical slot i % 4.  Each wave issues ROWS/64 of them.
+template <int ROWS, int AUX>
+__device__ __forceinline__ void stage_dma(rsrc_t rs, uint32_t ld_bytes, uint32_t col_bytes, char* region, int wave,
+                                          int lane) {
+#pragma unroll
+  for (int q = 0; q < ROWS / 64; ++q) {
+    const int r0 = wave * (ROWS / 4) + q * 16;
+    const int r = r0 + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    const uint32_t voff = (uint32_t)r * ld_bytes + col_bytes + (uint32_t)c * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LMCE_LDS_PTR(region + r0 * 64), 16, voff, 0, 0, AUX);
+  }
+}
+
+__device__ __forceinline__ bf16x8 stage_frag(const char* region, int row, int chunk) {
+  return *(const bf16x8*)(region + (row * 4 + (chunk ^ swz(row))) * 16);
+}
+
+// ------------------------------------------------------------------ GEMM
+// acc[mb][nb] += sum_k A[m][k] * B[n][k] over a BM x BN tile, 4 waves in a
+// 2 x 2 grid, each wave (wm, wn) owning rows wm*BM/2 + mb*32 + acc_row(.) and
+// columns wn*BN/2 + nb*32 + lane%32.  A and B are row-major bf16 with K
+// contiguous, reached through buffer resources (row stride lda/ldb bytes,
+// first column at acol/bcol bytes).  K % 32 == 0.  Four LDS stages are kept
+// in flight by LDS-DMA loads; one barrier per 32-wide K step.
+template <int BM, int BN, int AUXA>
+struct TileGemm {
+  static constexpr int BK = 32;
+  static constexpr int STAGES = 4;
+  static constexpr int MB = BM / 64;
+  static constexpr int NB = BN / 64;
+  static constexpr int LOADS = (BM + BN) / 64;   // DMA instructions per wave per stage
+  static constexpr int STAGE_BYTES = (BM + BN) * 64;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+
+  __device__ __forceinline__ static void issue(int kt, rsrc_t ra, uint32_t lda, uint32_t acol, rsrc_t rb,
+                                               uint32_t ldb, uint32_t bcol, char* lds, int wave, int lane) {
+    char* st = lds + (kt % STAGES) * STAGE_BYTES;
+    stage_dma<BM, AUXA>(ra, lda, acol + (uint32_t)kt * (BK * 2), st, wave, lane);
+    stage_dma<BN, 0>(rb, ldb, bcol + (uint32_t)kt * (BK * 2), st + BM * 64, wave, lane);
+  }
+
+  __device__ __forceinline__ static void run(rsrc_t ra, uint32_t lda, uint32_t acol, rsrc_t rb, uint32_t ldb,
+                                             uint32_t bcol, int K, char* lds, f32x16 (&acc)[MB][NB]) {
+    const int lane = lane_id();
+    const int wave = wave_id();
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = K / BK;
+    // Every earlier reader of this LDS is past this barrier, and no earlier
+    // vector memory operation of this wave is still counted in vmcnt.
+    wait_vmcnt<0>();
+    raw_barrier();
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(s, ra, lda, acol, rb, ldb, bcol, lds, wave, lane);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int later = nk - 1 - kt;  // stages issued after kt (capped at STAGES - 2)
+      if (later >= 2) wait_vmcnt<2 * LOADS>();
+      else if (later == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+      raw_barrier();
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, ra, lda, acol, rb, ldb, bcol, lds, wave, lane);
+      const char* sa = lds + (kt % STAGES) * STAGE_BYTES;
+      const char* sb = sa + BM * 64;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = 2 * ks + (lane >> 5);
+        bf16x8 fa[MB], fb[NB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) fa[mb] = stage_frag(sa, wm * (BM / 2) + mb * 32 + (lane & 31), c);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) fb[nb] = stage_frag(sb, wn * (BN / 2) + nb * 32 + (lane & 31), c);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa[mb], fb[nb], acc[mb][nb]);
+      }
+    }
+  }
+};
+
+template <int MB, int NB>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MB][NB]) {
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) zero(acc[i][j]);
+}
+
+__device__ __forceinline__ float pick16(const f32x16& x, int reg) {
+  float v = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v = (q == reg) ? x[q] : v;
+  return v;
+}
+
+__device__ __forceinline__ uint64_t pack_bf16x4(float a, float b, float c, float d) {
+  bf16x4 v = __builtin_convertvector((f32x4){a, b, c, d}, bf16x4);
+  return __builtin_bit_cast(uint64_t, v);
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte buffer store, coherent at device scope (seen by sc1 loads of other
+// workgroups once the storing wave has waited for it).  voff is per lane,
+// soff wave-uniform (kept in a scalar register).
+__device__ __forceinline__ void store_sc1_b64(rsrc_t rs, uint32_t voff, uint32_t soff, uint64_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, voff, soff, kAuxSc1);
+}
+
+// 4-byte buffer store (stores past the resource end are dropped).
+__device__ __forceinline__ void store_b32(rsrc_t rs, uint32_t voff, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, soff, 0);
+}
+
+// Writes a BM x BN fp32 accumulator tile (the layout of TileGemm) to a
+// row-major matrix whose element (0, 0) is at `base`; rows at or past
+// `rows_left` are skipped.  Address parts that are the same for the whole
+// wave go in the scalar offset; a skipped row gets a vector offset past the
+// resource end (the range check applies to the vector offset), so its store
+// is dropped.
+template <int MB, int NB>
+__device__ __forceinline__ void store_tile_f32(float* base, int64_t rows_left, int64_t ld, int64_t cols_left,
+                                               const f32x16 (&acc)[MB][NB], int row0, int col0, int lane) {
+  const rsrc_t rs = make_rsrc(base, (uint64_t)((rows_left - 1) * ld + cols_left) * 4);
+  lane = lane_id();
+  const int lrow = (lane >> 5) << 2;  // row offset of this lane half
+  const uint32_t voff = (uint32_t)((lrow * ld + (lane & 31)) * 4);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int reg = 0; reg < 16; ++reg) {
+        const int rr = row0 + mb * 32 + ((reg >> 2) << 3) + (reg & 3);
+        const uint32_t soff = (uint32_t)(((int64_t)rr * ld + col0 + nb * 32) * 4);
+        const uint32_t v = (rr + lrow < rows_left) ? voff : 0xfffffff0u;
+        store_b32(rs, v, soff, acc[mb][nb][reg]);
+      }
+}
+
+}  // namespace lmce

@@ -1,5 +1,5 @@
 // Internal declarations shared by the host planner (lmce_api.hip) and the
-// device kernels (lmce_kernels.hip).  Not part of the public C ABI.
+// device kernels (lmce_fwd.hip, lmce_bwd.hip).  Not part of the public C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,14 +7,18 @@
 
 namespace lmce {
 
-constexpr int kStatusLabel = 1;   // asynchronous flag: a label was out of range
-constexpr int kTile = 128;        // rows of h / W in one logit tile
-constexpr int kStageK = 64;       // hidden-size granularity of the main loop
+constexpr int kStatusLabel = 1;     // asynchronous flag: a label was out of range
+constexpr int kStatusSync = 2;      // asynchronous flag: a group wait timed out
+constexpr int kStageK = 64;         // hidden-size granularity
+constexpr int kVTile = 256;         // vocabulary rows per forward logit tile
+constexpr int kSyncStride = 64;     // u32 words between two groups' counters (256 bytes)
+constexpr int kMaxBwdWGs = 256;     // upper bound of a backward cooperative grid
+constexpr int kXbufPerWG = 2 * 256 * 128 * 2;  // exchange bytes per backward workgroup
 
 // First 256 bytes of the workspace.
 struct WsHeader {
   int n_valid;   // rows whose label is not ignore_index (and is in range)
-  int status;    // 0 or kStatusLabel
+  int status;    // 0, or kStatusLabel | kStatusSync
   int pad[62];
 };
 
@@ -24,16 +28,18 @@ struct FwdArgs {
   const int64_t* labels;
   int64_t L, H, V, ignore_index;
   int chunk_rows;       // rows per schedule chunk
-  int tiles_per_chunk;  // ceil(chunk_rows / 128)
-  int n_chunks;         // ceil(L / chunk_rows)
+  int tile_rows;        // tokens per workgroup tile (128 or 256)
+  int tiles_per_chunk;  // ceil(chunk_rows / tile_rows)
+  int ntiles;           // row tiles over all chunks
   int segments;         // vocabulary segments swept by separate workgroups
-  int vtiles;           // ceil(V / 128)
-  int vtiles_per_seg;   // ceil(vtiles / segments)
+  int vtiles;           // ceil(V / 256)
+  int vtiles_per_seg;   // vocabulary tiles per segment
+  int xcd_map;          // 1: XCD-aware item order (8 segments, ntiles % 32 == 0)
   WsHeader* hdr;
-  float* zlabel;        // [L] logit of each row's label
+  float* zlabel;        // (unused) reserved
   float* part_m;        // [segments][L] running max per row and segment
   float* part_s;        // [segments][L] sum of exp(z - max) per row and segment
-  float* block_sum;     // [ceil(L/256)] per-block nll sums
+  float* block_sum;     // [ceil(L/64)] per-block nll sums
 };
 
 struct BwdArgs {
@@ -45,7 +51,11 @@ struct BwdArgs {
   const uint16_t* hT;   // [H][Lpad] transposed h, zero past L
   const uint16_t* WT;   // [H][Vpad] transposed W, zero past V
   int64_t L, H, V, ignore_index, Lpad, Vpad;
-  int vtiles;
+  int group_size;       // workgroups per group = H / HS
+  int n_groups;
+  int spin_limit;       // bound of every group wait
+  unsigned* sync;       // [n_groups * kSyncStride] arrival counters, zeroed before the launch
+  uint16_t* xbuf;       // [n_groups][2][256][group_size * 128] exchange slots
   WsHeader* hdr;
   float* dh;
   float* dW;
@@ -55,7 +65,8 @@ hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int6
                                hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
 hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st);
-hipError_t launch_bwd_dh(const BwdArgs& a, int hs, hipStream_t st);
-hipError_t launch_bwd_dW(const BwdArgs& a, int hs, hipStream_t st);
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
+hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs);
+hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int hs, int n_wgs, hipStream_t st);
 
 }  // namespace lmce
