@@ -126,9 +126,6 @@ def main():
         step()
         torch.cuda.synchronize()
         log(f"[bench] warmup {i + 1}/{args.warmup} done")
-    if lm.lmce_read_status(ws) != _lib.LMCE_OK:
-        raise RuntimeError("label status error")
-
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -136,6 +133,9 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    status = lm.lmce_read_status(ws)
+    if status != _lib.LMCE_OK:
+        raise RuntimeError(f"lmce status {status}: {_lib.strerror(status)}")
     peak_extra = torch.cuda.max_memory_allocated(dev) - base_alloc
     fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
     dh_ms = [e[1].elapsed_time(e[2]) for e in events]

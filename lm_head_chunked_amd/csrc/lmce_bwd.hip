@@ -29,8 +29,10 @@
 
 namespace lmce {
 
-// out[c][r] = in[r][c] for r < R, 0 for R <= r < Rpad.  in is [R x C]
-// row-major, out is [C x Rpad].  64x64 tiles through LDS; C % 64 == 0.
+// Tile-major transpose: out holds, for each 128-row tile t of `in`, the
+// block [C][128] with out[(t*C + c)*128 + rr] = in[t*128 + rr][c] (0 past R).
+// A consumer slice (consecutive c) of one tile is then one contiguous block.
+// 64x64 tiles through LDS; C % 64 == 0, Rpad % 128 == 0.
 __global__ __launch_bounds__(256) void k_transpose(const u16* __restrict__ in, int64_t R, int64_t C,
                                                    u16* __restrict__ out, int64_t Rpad) {
   __shared__ u16 t[64][66];
@@ -42,9 +44,11 @@ __global__ __launch_bounds__(256) void k_transpose(const u16* __restrict__ in, i
     t[rr][cc] = (r < R) ? in[r * C + c0 + cc] : (u16)0;
   }
   __syncthreads();
+  const int64_t tile = r0 >> 7;
+  const int64_t rin = r0 & 127;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int cc = i >> 6, rr = i & 63;
-    out[(c0 + cc) * Rpad + r0 + rr] = t[rr][cc];
+    out[(tile * C + c0 + cc) * 128 + rin + rr] = t[rr][cc];
   }
 }
 
@@ -94,7 +98,7 @@ __device__ __forceinline__ bool group_arrive_wait(unsigned* ctr, unsigned target
 template <int HS>
 __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
   using P = TileGemm<128, 256, 0>;       // producer: 128 vocabulary x 256 tokens
-  using C = TileGemm<256, HS, kAuxSc1>;  // consumer: 256 tokens x HS columns
+  using C = TileGemm<256, HS, kAuxSc1, 1, 1>;  // consumer: 256 tokens x HS columns, K-tiled operands
   constexpr int LDS = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   __shared__ int s_flag;
@@ -107,9 +111,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t H = p.H, V = p.V, L = p.L;
   const int64_t c0 = (int64_t)j * HS;
-  const int64_t ldx = (int64_t)s * 128;  // slot row length (elements)
+  const int64_t slot_elems = (int64_t)s * 256 * 128;  // slot = s tiles of [256][128]
   // per-lane part of an exchange store: row lane%32, 4 columns per lane half
-  const uint32_t xvoff = (uint32_t)(((lane & 31) * ldx + ((lane >> 5) << 2)) * 2);
+  const uint32_t xvoff = (uint32_t)(((lane & 31) * 128 + ((lane >> 5) << 2)) * 2);
   const int vt128 = (int)((V + 127) / 128);
   const int rounds = (vt128 + s - 1) / s;
   const int nrb = (int)((L + 255) / 256);
@@ -132,23 +136,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
       scale[nb] = valid ? gscale : 0.f;
       lse2[nb] = t < rend ? p.lse[t] * kLog2e : INFINITY;  // rows past L: probability 0
     }
-    const rsrc_t rh = make_rsrc(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2);
+    const Operand oh = linear_operand(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
 
     f32x16 dacc[C::MB][C::NB];
     zero_acc(dacc);
     for (int k = 0; k < rounds; ++k, ++epoch) {
-      u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * 256 * ldx;
-      const rsrc_t rslot = make_rsrc(slot, (uint64_t)256 * ldx * 2);
+      u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
+      const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
       const int vt = k * s + j;
       if (vt < vt128) {
         const int64_t v0 = (int64_t)vt * 128;
         f32x16 z[P::MB][P::NB];
         zero_acc(z);
-        P::run(make_rsrc(p.W + v0 * H, (uint64_t)(V - v0) * H * 2), (uint32_t)(H * 2), 0, rh, (uint32_t)(H * 2), 0,
-               (int)H, lds, z);
+        P::run(linear_operand(p.W + v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2)), oh, (int)H, lds, z);
         // G[token][v] = scale * (exp(z - lse) - [v == y]); 4 consecutive v per store.
         // Tile-local 32-bit coordinates: vl = v - v0, label at lab - v0.
         const int vlim = (int)min<int64_t>(V - v0, 128);
+        const int jo = opaque_s(j);  // keeps the store offsets below from being hoisted out of the loop
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int tl = wn * 128 + nb * 32 + (lane & 31);
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
                 pr = (vl0 + e == yl) ? pr - 1.f : pr;
                 gv[e] = pr * ((vl0 + e < vlim) ? scale[nb] : 0.f);
               }
-              const uint32_t soff = (uint32_t)(((wn * 128 + nb * 32) * ldx + j * 128 + wm * 64 + mb * 32 + qq * 8) * 2);
+              const uint32_t soff = (uint32_t)((((int64_t)jo * 256 + wn * 128 + nb * 32) * 128 + wm * 64 + mb * 32 + qq * 8) * 2);
               store_sc1_b64(rslot, xvoff, soff, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
             }
           __builtin_amdgcn_sched_barrier(0);
@@ -176,8 +180,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
         return;
       const int ntl = min(s, vt128 - k * s);
       const int64_t vbase = (int64_t)k * s * 128;
-      C::run(make_rsrc(slot, (uint64_t)256 * ldx * 2), (uint32_t)(ldx * 2), 0,
-             make_rsrc(p.WT + c0 * p.Vpad + vbase, (uint64_t)HS * p.Vpad * 2), (uint32_t)(p.Vpad * 2), 0, ntl * 128,
+      // A: the slot's tiles [256][128] (K-tiled); B: W^T tiles [H][128] of the
+      // round's vocabulary, rows c0 .. c0+HS (K-tiled)
+      C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
+             tiled_operand(p.WT + (vbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
              lds, dacc);
     }
     // dh[r][c] for r < L (waves: wm token half, wn column half)
@@ -194,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
 template <int HS>
 __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
   using P = TileGemm<128, 256, 0>;       // producer: 128 tokens x 256 vocabulary
-  using C = TileGemm<256, HS, kAuxSc1>;  // consumer: 256 vocabulary x HS columns
+  using C = TileGemm<256, HS, kAuxSc1, 1, 1>;  // consumer: 256 vocabulary x HS columns, K-tiled operands
   constexpr int LDS = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   __shared__ float row_lse2[128], row_scale[128];
@@ -209,8 +215,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t H = p.H, V = p.V, L = p.L;
   const int64_t c0 = (int64_t)j * HS;
-  const int64_t ldx = (int64_t)s * 128;
-  const uint32_t xvoff = (uint32_t)(((lane & 31) * ldx + ((lane >> 5) << 2)) * 2);
+  const int64_t slot_elems = (int64_t)s * 256 * 128;
+  const uint32_t xvoff = (uint32_t)(((lane & 31) * 128 + ((lane >> 5) << 2)) * 2);
   const int rt128 = (int)((L + 127) / 128);
   const int rounds = (rt128 + s - 1) / s;
   const int nvb = (int)((V + 255) / 256);
@@ -220,12 +226,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
 
   for (int vb = g; vb < nvb; vb += p.n_groups) {
     const int64_t v0 = (int64_t)vb * 256;
-    const rsrc_t rw = make_rsrc(p.W + v0 * H, (uint64_t)(V - v0) * H * 2);
+    const Operand ow = linear_operand(p.W + v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
     f32x16 dacc[C::MB][C::NB];
     zero_acc(dacc);
     for (int k = 0; k < rounds; ++k, ++epoch) {
-      u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * 256 * ldx;
-      const rsrc_t rslot = make_rsrc(slot, (uint64_t)256 * ldx * 2);
+      u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
+      const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
       const int rt = k * s + j;
       if (rt < rt128) {
         const int64_t r0 = (int64_t)rt * 128;
@@ -241,12 +247,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
         f32x16 z[P::MB][P::NB];
         zero_acc(z);
         // (the GEMM's first barrier orders the row_* writes before their use)
-        P::run(make_rsrc(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2), (uint32_t)(H * 2), 0, rw, (uint32_t)(H * 2),
-               0, (int)H, lds, z);
+        P::run(linear_operand(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2)), ow, (int)H, lds, z);
         // G^T[v][token]: lane = v (column), 4 consecutive tokens per store.
         // Token data is read once per 4-token group and reused for the
         // lane's 4 vocabulary columns; columns past V get a zero factor.
         const int vlim = (int)min<int64_t>(V - v0, 256);
+        const int jo = opaque_s(j);  // keeps the store offsets below from being hoisted out of the loop
         float vmask[4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) vmask[nb] = (wn * 128 + nb * 32 + (lane & 31) < vlim) ? 1.f : 0.f;
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
                 pr = (vl == tlab[e]) ? pr - 1.f : pr;
                 gv[e] = pr * (tsc[e] * vmask[nb]);
               }
-              const uint32_t soff = (uint32_t)(((wn * 128 + nb * 32) * ldx + j * 128 + wm * 64 + mb * 32 + qq * 8) * 2);
+              const uint32_t soff = (uint32_t)((((int64_t)jo * 256 + wn * 128 + nb * 32) * 128 + wm * 64 + mb * 32 + qq * 8) * 2);
               store_sc1_b64(rslot, xvoff, soff, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -283,8 +289,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
         return;
       const int ntl = min(s, rt128 - k * s);
       const int64_t rbase = (int64_t)k * s * 128;
-      C::run(make_rsrc(slot, (uint64_t)256 * ldx * 2), (uint32_t)(ldx * 2), 0,
-             make_rsrc(p.hT + c0 * p.Lpad + rbase, (uint64_t)HS * p.Lpad * 2), (uint32_t)(p.Lpad * 2), 0, ntl * 128,
+      C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
+             tiled_operand(p.hT + (rbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
              lds, dacc);
     }
     store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, dacc, wm * 128, wn * (HS / 2), lane);

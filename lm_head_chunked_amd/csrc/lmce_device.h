@@ -38,6 +38,13 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // (scalar register), so that addresses built from it stay scalar.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// A wave-uniform value hidden from loop-invariant code motion (kept in a
+// scalar register): expressions built from it are recomputed where used.
+__device__ __forceinline__ int opaque_s(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 // The lane index, hidden from loop-invariant code motion: addresses derived
 // from it are recomputed where they are used instead of being hoisted out of
 // the long loops and kept live in registers.
@@ -101,18 +108,65 @@ __device__ __forceinline__ void stage_dma(rsrc_t rs, uint32_t ld_bytes, uint32_t
   }
 }
 
+// Fragment read from a stage through inline asm: the compiler's LDS-DMA
+// bookkeeping would otherwise put a full vmcnt(0) wait in front of every LDS
+// read and serialise the prefetch pipeline.  The caller waits for the reads
+// with lds_wait_frags() before using the fragments.
 __device__ __forceinline__ bf16x8 stage_frag(const char* region, int row, int chunk) {
-  return *(const bf16x8*)(region + (row * 4 + (chunk ^ swz(row))) * 16);
+  const char* p = region + (row * 4 + (chunk ^ swz(row))) * 16;
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  bf16x8 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+
+// Waits for every outstanding LDS read of this wave.  The fragments are
+// tied to the wait so that no instruction using them is scheduled before it.
+template <int MB, int NB>
+__device__ __forceinline__ void lds_wait_frags(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
+  static_assert(MB + NB <= 8, "at most 8 fragments per wait");
+  if constexpr (MB == 4 && NB == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]),
+                 "+v"(fb[2]), "+v"(fb[3]));
+  else if constexpr (MB == 4 && NB == 2)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]));
+  else if constexpr (MB == 2 && NB == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]), "+v"(fb[3]));
+  else if constexpr (MB == 4 && NB == 1)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]));
+  else if constexpr (MB == 2 && NB == 2)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]), "+v"(fb[1]));
+  else if constexpr (MB == 2 && NB == 1)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]));
+  else
+    static_assert(MB == 0, "unsupported fragment count");
 }
 
 // ------------------------------------------------------------------ GEMM
 // acc[mb][nb] += sum_k A[m][k] * B[n][k] over a BM x BN tile, 4 waves in a
 // 2 x 2 grid, each wave (wm, wn) owning rows wm*BM/2 + mb*32 + acc_row(.) and
-// columns wn*BN/2 + nb*32 + lane%32.  A and B are row-major bf16 with K
-// contiguous, reached through buffer resources (row stride lda/ldb bytes,
-// first column at acol/bcol bytes).  K % 32 == 0.  Four LDS stages are kept
+// columns wn*BN/2 + nb*32 + lane%32.  A and B are bf16 with K contiguous,
+// reached through buffer resources.  K % 32 == 0.  Four LDS stages are kept
 // in flight by LDS-DMA loads; one barrier per 32-wide K step.
-template <int BM, int BN, int AUXA>
+//
+// Operand addressing (bytes from the resource base): row r, K index k is at
+//   linear  (KT == 0):  r * ld + col + 2k
+//   K-tiled (KT == 1):  (k / 128) * tstride + r * ld + 2 (k % 128)
+// The K-tiled form reads matrices stored as consecutive [rows][128] blocks.
+struct Operand {
+  rsrc_t rs;
+  uint32_t ld;       // bytes between rows
+  uint32_t col;      // linear: byte offset of the first K column
+  uint32_t tstride;  // K-tiled: bytes between 128-wide K blocks
+};
+
+template <int KT>
+__device__ __forceinline__ uint32_t k_offset(const Operand& o, int kt) {
+  if constexpr (KT == 0) return o.col + (uint32_t)kt * 64u;
+  else return (uint32_t)(kt >> 2) * o.tstride + (uint32_t)(kt & 3) * 64u;
+}
+
+template <int BM, int BN, int AUXA, int KTA = 0, int KTB = 0>
 struct TileGemm {
   static constexpr int BK = 32;
   static constexpr int STAGES = 4;
@@ -122,15 +176,15 @@ struct TileGemm {
   static constexpr int STAGE_BYTES = (BM + BN) * 64;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
 
-  __device__ __forceinline__ static void issue(int kt, rsrc_t ra, uint32_t lda, uint32_t acol, rsrc_t rb,
-                                               uint32_t ldb, uint32_t bcol, char* lds, int wave, int lane) {
+  __device__ __forceinline__ static void issue(int kt, const Operand& a, const Operand& b, char* lds, int wave,
+                                               int lane) {
     char* st = lds + (kt % STAGES) * STAGE_BYTES;
-    stage_dma<BM, AUXA>(ra, lda, acol + (uint32_t)kt * (BK * 2), st, wave, lane);
-    stage_dma<BN, 0>(rb, ldb, bcol + (uint32_t)kt * (BK * 2), st + BM * 64, wave, lane);
+    stage_dma<BM, AUXA>(a.rs, a.ld, k_offset<KTA>(a, kt), st, wave, lane);
+    stage_dma<BN, 0>(b.rs, b.ld, k_offset<KTB>(b, kt), st + BM * 64, wave, lane);
   }
 
-  __device__ __forceinline__ static void run(rsrc_t ra, uint32_t lda, uint32_t acol, rsrc_t rb, uint32_t ldb,
-                                             uint32_t bcol, int K, char* lds, f32x16 (&acc)[MB][NB]) {
+  __device__ __forceinline__ static void run(const Operand& a, const Operand& b, int K, char* lds,
+                                             f32x16 (&acc)[MB][NB]) {
     const int lane = lane_id();
     const int wave = wave_id();
     const int wm = wave >> 1, wn = wave & 1;
@@ -141,14 +195,14 @@ struct TileGemm {
     raw_barrier();
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) issue(s, ra, lda, acol, rb, ldb, bcol, lds, wave, lane);
+      if (s < nk) issue(s, a, b, lds, wave, lane);
     for (int kt = 0; kt < nk; ++kt) {
       const int later = nk - 1 - kt;  // stages issued after kt (capped at STAGES - 2)
       if (later >= 2) wait_vmcnt<2 * LOADS>();
       else if (later == 1) wait_vmcnt<LOADS>();
       else wait_vmcnt<0>();
       raw_barrier();
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, ra, lda, acol, rb, ldb, bcol, lds, wave, lane);
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, a, b, lds, wave, lane);
       const char* sa = lds + (kt % STAGES) * STAGE_BYTES;
       const char* sb = sa + BM * 64;
 #pragma unroll
@@ -159,6 +213,7 @@ struct TileGemm {
         for (int mb = 0; mb < MB; ++mb) fa[mb] = stage_frag(sa, wm * (BM / 2) + mb * 32 + (lane & 31), c);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) fb[nb] = stage_frag(sb, wn * (BN / 2) + nb * 32 + (lane & 31), c);
+        lds_wait_frags(fa, fb);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -167,6 +222,24 @@ struct TileGemm {
     }
   }
 };
+
+__device__ __forceinline__ Operand linear_operand(const void* base, uint64_t bytes, uint32_t ld, uint32_t col = 0) {
+  Operand o;
+  o.rs = make_rsrc(base, bytes);
+  o.ld = ld;
+  o.col = col;
+  o.tstride = 0;
+  return o;
+}
+
+__device__ __forceinline__ Operand tiled_operand(const void* base, uint64_t bytes, uint32_t ld, uint32_t tstride) {
+  Operand o;
+  o.rs = make_rsrc(base, bytes);
+  o.ld = ld;
+  o.col = 0;
+  o.tstride = tstride;
+  return o;
+}
 
 template <int MB, int NB>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[MB][NB]) {
@@ -213,6 +286,7 @@ __device__ __forceinline__ void store_tile_f32(float* base, int64_t rows_left, i
                                                const f32x16 (&acc)[MB][NB], int row0, int col0, int lane) {
   const rsrc_t rs = make_rsrc(base, (uint64_t)((rows_left - 1) * ld + cols_left) * 4);
   lane = lane_id();
+  row0 = opaque_s(row0);
   const int lrow = (lane >> 5) << 2;  // row offset of this lane half
   const uint32_t voff = (uint32_t)((lrow * ld + (lane & 31)) * 4);
 #pragma unroll

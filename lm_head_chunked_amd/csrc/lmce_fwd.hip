@@ -126,8 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd(FwdArgs p) {
     m[nb] = kNegBig;
     sum[nb] = 0.f;
   }
-  const rsrc_t rb = make_rsrc(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2);
-  const uint32_t ldb = (uint32_t)(H * 2);
+  const Operand ob = linear_operand(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
 
   const int vt0 = seg * p.vtiles_per_seg;
   const int vt1 = min(vt0 + p.vtiles_per_seg, p.vtiles);
@@ -135,10 +134,10 @@ __global__ __launch_bounds__(kThreads) void k_fwd(FwdArgs p) {
     const int64_t v0 = (int64_t)vt * 256;
     // A = W rows (vocabulary on the MFMA M side), B = h rows (tokens on N):
     // every logit of a token sits in the registers of one lane pair.
-    const rsrc_t ra = make_rsrc(p.W + v0 * H, (uint64_t)(V - v0) * H * 2);
+    const Operand oa = linear_operand(p.W + v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
     f32x16 acc[4][NB];
     zero_acc(acc);
-    G::run(ra, ldb, 0, rb, ldb, 0, (int)H, lds, acc);
+    G::run(oa, ob, (int)H, lds, acc);
 
     if (v0 + 256 <= V) fold_tile<NB, false>(acc, m, sum, 0, lane);
     else fold_tile<NB, true>(acc, m, sum, (int)(V - (v0 + wm * 128)), lane);  // ragged last tile

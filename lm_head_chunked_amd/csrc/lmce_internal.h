@@ -48,14 +48,14 @@ struct BwdArgs {
   const int64_t* labels;
   const float* lse;
   const float* grad_loss;
-  const uint16_t* hT;   // [H][Lpad] transposed h, zero past L
-  const uint16_t* WT;   // [H][Vpad] transposed W, zero past V
+  const uint16_t* hT;   // h transposed tile-major: [Lpad/128][H][128], zero past L
+  const uint16_t* WT;   // W transposed tile-major: [Vpad/128][H][128], zero past V
   int64_t L, H, V, ignore_index, Lpad, Vpad;
   int group_size;       // workgroups per group = H / HS
   int n_groups;
   int spin_limit;       // bound of every group wait
   unsigned* sync;       // [n_groups * kSyncStride] arrival counters, zeroed before the launch
-  uint16_t* xbuf;       // [n_groups][2][256][group_size * 128] exchange slots
+  uint16_t* xbuf;       // [n_groups][2][group_size][256][128] exchange slots
   WsHeader* hdr;
   float* dh;
   float* dW;
