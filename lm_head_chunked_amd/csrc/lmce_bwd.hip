@@ -97,8 +97,8 @@ __device__ __forceinline__ bool group_arrive_wait(unsigned* ctr, unsigned target
 // with K = 128 * (tiles in the round).
 template <int HS>
 __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
-  using P = TileGemm<128, 256, 0>;       // producer: 128 vocabulary x 256 tokens
-  using C = TileGemm<256, HS, kAuxSc1, 1, 1>;  // consumer: 256 tokens x HS columns, K-tiled operands
+  using P = TileGemm<128, 256, 2, 2>;    // producer: 128 vocabulary x 256 tokens
+  using C = TileGemm<256, HS, 2, 2, kAuxSc1, 1, 1>;  // consumer: 256 tokens x HS columns, K-tiled operands
   constexpr int LDS = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   __shared__ int s_flag;
@@ -199,8 +199,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
 //   dW[v rows][c0 .. c0+HS] += slot[256][K] * h^T[c0 .. c0+HS][round's tokens].
 template <int HS>
 __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
-  using P = TileGemm<128, 256, 0>;       // producer: 128 tokens x 256 vocabulary
-  using C = TileGemm<256, HS, kAuxSc1, 1, 1>;  // consumer: 256 vocabulary x HS columns, K-tiled operands
+  using P = TileGemm<128, 256, 2, 2>;    // producer: 128 tokens x 256 vocabulary
+  using C = TileGemm<256, HS, 2, 2, kAuxSc1, 1, 1>;  // consumer: 256 vocabulary x HS columns, K-tiled operands
   constexpr int LDS = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   __shared__ float row_lse2[128], row_scale[128];

@@ -94,13 +94,15 @@ __device__ __forceinline__ void raw_barrier() {
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
 
 // One wave-level LDS-DMA load moves 1 KiB: lane i lands at lds_base + 16*i,
-// i.e. rows r0 .. r0+15, physical slot i % 4.  Each wave issues ROWS/64 of them.
-template <int ROWS, int AUX>
+// i.e. rows r0 .. r0+15, physical slot i % 4.  The NW waves of the
+// workgroup issue ROWS/16/NW of them each.
+template <int ROWS, int NW, int AUX>
 __device__ __forceinline__ void stage_dma(rsrc_t rs, uint32_t ld_bytes, uint32_t col_bytes, char* region, int wave,
                                           int lane) {
+  static_assert(ROWS % (16 * NW) == 0, "rows per stage must split evenly over the waves");
 #pragma unroll
-  for (int q = 0; q < ROWS / 64; ++q) {
-    const int r0 = wave * (ROWS / 4) + q * 16;
+  for (int q = 0; q < ROWS / 16 / NW; ++q) {
+    const int r0 = (wave * (ROWS / 16 / NW) + q) * 16;
     const int r = r0 + (lane >> 2);
     const int c = (lane & 3) ^ swz(r);
     const uint32_t voff = (uint32_t)r * ld_bytes + col_bytes + (uint32_t)c * 16u;
@@ -143,9 +145,9 @@ __device__ __forceinline__ void lds_wait_frags(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB
 }
 
 // ------------------------------------------------------------------ GEMM
-// acc[mb][nb] += sum_k A[m][k] * B[n][k] over a BM x BN tile, 4 waves in a
-// 2 x 2 grid, each wave (wm, wn) owning rows wm*BM/2 + mb*32 + acc_row(.) and
-// columns wn*BN/2 + nb*32 + lane%32.  A and B are bf16 with K contiguous,
+// acc[mb][nb] += sum_k A[m][k] * B[n][k] over a BM x BN tile, WM x WN waves,
+// each wave (wm, wn) owning rows wm*BM/WM + mb*32 + acc_row(.) and columns
+// wn*BN/WN + nb*32 + lane%32.  A and B are bf16 with K contiguous,
 // reached through buffer resources.  K % 32 == 0.  Four LDS stages are kept
 // in flight by LDS-DMA loads; one barrier per 32-wide K step.
 //
@@ -166,28 +168,30 @@ __device__ __forceinline__ uint32_t k_offset(const Operand& o, int kt) {
   else return (uint32_t)(kt >> 2) * o.tstride + (uint32_t)(kt & 3) * 64u;
 }
 
-template <int BM, int BN, int AUXA, int KTA = 0, int KTB = 0>
+template <int BM, int BN, int WM, int WN, int AUXA = 0, int KTA = 0, int KTB = 0>
 struct TileGemm {
+  static constexpr int NW = WM * WN;             // waves
+  static constexpr int NT = 64 * NW;             // threads
   static constexpr int BK = 32;
   static constexpr int STAGES = 4;
-  static constexpr int MB = BM / 64;
-  static constexpr int NB = BN / 64;
-  static constexpr int LOADS = (BM + BN) / 64;   // DMA instructions per wave per stage
+  static constexpr int MB = BM / WM / 32;        // 32-row blocks per wave
+  static constexpr int NB = BN / WN / 32;        // 32-column blocks per wave
+  static constexpr int LOADS = (BM + BN) / 16 / NW;  // DMA instructions per wave per stage
   static constexpr int STAGE_BYTES = (BM + BN) * 64;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
 
   __device__ __forceinline__ static void issue(int kt, const Operand& a, const Operand& b, char* lds, int wave,
                                                int lane) {
     char* st = lds + (kt % STAGES) * STAGE_BYTES;
-    stage_dma<BM, AUXA>(a.rs, a.ld, k_offset<KTA>(a, kt), st, wave, lane);
-    stage_dma<BN, 0>(b.rs, b.ld, k_offset<KTB>(b, kt), st + BM * 64, wave, lane);
+    stage_dma<BM, NW, AUXA>(a.rs, a.ld, k_offset<KTA>(a, kt), st, wave, lane);
+    stage_dma<BN, NW, 0>(b.rs, b.ld, k_offset<KTB>(b, kt), st + BM * 64, wave, lane);
   }
 
   __device__ __forceinline__ static void run(const Operand& a, const Operand& b, int K, char* lds,
                                              f32x16 (&acc)[MB][NB]) {
     const int lane = lane_id();
     const int wave = wave_id();
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int nk = K / BK;
     // Every earlier reader of this LDS is past this barrier, and no earlier
     // vector memory operation of this wave is still counted in vmcnt.
@@ -210,9 +214,9 @@ struct TileGemm {
         const int c = 2 * ks + (lane >> 5);
         bf16x8 fa[MB], fb[NB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) fa[mb] = stage_frag(sa, wm * (BM / 2) + mb * 32 + (lane & 31), c);
+        for (int mb = 0; mb < MB; ++mb) fa[mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), c);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fb[nb] = stage_frag(sb, wn * (BN / 2) + nb * 32 + (lane & 31), c);
+        for (int nb = 0; nb < NB; ++nb) fb[nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), c);
         lds_wait_frags(fa, fb);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)

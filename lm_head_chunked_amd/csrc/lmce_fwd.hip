@@ -63,18 +63,18 @@ __device__ __forceinline__ void fwd_item(int i, const FwdArgs& p, int& tile, int
   }
 }
 
-// Folds one 256 x BN logit tile into the lane's running (max, sum) states.
-// Lane l holds, for each of its NB tokens, 64 logits (4 blocks x 16 rows).
+// Folds one logit tile into the lane's running (max, sum) states.  Lane l
+// holds, for each of its NB tokens, MB*16 logits (MB blocks x 16 rows).
 // MASK: rows at or past `valid_rows` (counted from this wave's first
 // vocabulary row) lie beyond V and are skipped.
-template <int NB, bool MASK>
-__device__ __forceinline__ void fold_tile(const f32x16 (&acc)[4][NB], float (&m)[NB], float (&sum)[NB],
+template <int MB, int NB, bool MASK>
+__device__ __forceinline__ void fold_tile(const f32x16 (&acc)[MB][NB], float (&m)[NB], float (&sum)[NB],
                                           int valid_rows, int lane) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float mt = kNegBig;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const bool in = !MASK || (mb * 32 + acc_row(r, lane) < valid_rows);
@@ -84,7 +84,7 @@ __device__ __forceinline__ void fold_tile(const f32x16 (&acc)[4][NB], float (&m)
     const float off = -mn * kLog2e;
     float add = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = exp2_fast(__builtin_fmaf(acc[mb][nb][r], kLog2e, off));
@@ -97,12 +97,16 @@ __device__ __forceinline__ void fold_tile(const f32x16 (&acc)[4][NB], float (&m)
   }
 }
 
+// 8 waves (2 per SIMD) in a 4 (vocabulary) x 2 (token) grid over a 256 x BN
+// logit tile: each wave holds 64 vocabulary rows of BN/2 tokens.
+constexpr int kFwdWM = 4, kFwdWN = 2, kFwdThreads = 64 * kFwdWM * kFwdWN;
+
 template <int BN>
-__global__ __launch_bounds__(kThreads) void k_fwd(FwdArgs p) {
-  using G = TileGemm<256, BN, 0>;
-  constexpr int NB = G::NB;
+__global__ __launch_bounds__(kFwdThreads) void k_fwd(FwdArgs p) {
+  using G = TileGemm<256, BN, kFwdWM, kFwdWN>;
+  constexpr int MB = G::MB, NB = G::NB;
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-  __shared__ float red_m[BN], red_s[BN];
+  __shared__ float red_m[kFwdWM - 1][BN], red_s[kFwdWM - 1][BN];
 
   int tile, seg;
   fwd_item(blockIdx.x, p, tile, seg);
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd(FwdArgs p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kFwdWN, wn = wave % kFwdWN;
   const int64_t H = p.H, V = p.V;
 
   int64_t tok[NB];
@@ -133,37 +137,38 @@ __global__ __launch_bounds__(kThreads) void k_fwd(FwdArgs p) {
   for (int vt = vt0; vt < vt1; ++vt) {
     const int64_t v0 = (int64_t)vt * 256;
     // A = W rows (vocabulary on the MFMA M side), B = h rows (tokens on N):
-    // every logit of a token sits in the registers of one lane pair.
+    // every logit of a token sits in the registers of one lane pair per wave.
     const Operand oa = linear_operand(p.W + v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
-    f32x16 acc[4][NB];
+    f32x16 acc[MB][NB];
     zero_acc(acc);
     G::run(oa, ob, (int)H, lds, acc);
-
-    if (v0 + 256 <= V) fold_tile<NB, false>(acc, m, sum, 0, lane);
-    else fold_tile<NB, true>(acc, m, sum, (int)(V - (v0 + wm * 128)), lane);  // ragged last tile
+    if (v0 + 256 <= V) fold_tile<MB, NB, false>(acc, m, sum, 0, lane);
+    else fold_tile<MB, NB, true>(acc, m, sum, (int)(V - (v0 + wm * 64)), lane);  // ragged last tile
   }
 
   // Merge the two lane halves (same tokens, other vocabulary rows), then the
-  // two waves that share tokens; one (max, sum) pair per token and segment.
+  // four waves that share tokens, in wave order; one (max, sum) pair per
+  // token and segment.
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float m2 = __shfl_xor(m[nb], 32);
     const float s2 = __shfl_xor(sum[nb], 32);
     lse_merge(m[nb], sum[nb], m2, s2);
   }
-  __syncthreads();
-  if (wm == 1 && lane < 32) {
+  if (wm > 0 && lane < 32) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      red_m[wn * (BN / 2) + nb * 32 + lane] = m[nb];
-      red_s[wn * (BN / 2) + nb * 32 + lane] = sum[nb];
+      red_m[wm - 1][wn * (BN / 2) + nb * 32 + lane] = m[nb];
+      red_s[wm - 1][wn * (BN / 2) + nb * 32 + lane] = sum[nb];
     }
   }
   __syncthreads();
   if (wm == 0 && lane < 32) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      lse_merge(m[nb], sum[nb], red_m[wn * (BN / 2) + nb * 32 + lane], red_s[wn * (BN / 2) + nb * 32 + lane]);
+      const int t = wn * (BN / 2) + nb * 32 + lane;
+#pragma unroll
+      for (int w = 0; w < kFwdWM - 1; ++w) lse_merge(m[nb], sum[nb], red_m[w][t], red_s[w][t]);
       if (tok[nb] < rend) {
         p.part_m[(int64_t)seg * p.L + tok[nb]] = m[nb];
         p.part_s[(int64_t)seg * p.L + tok[nb]] = sum[nb];
@@ -247,8 +252,8 @@ hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int6
 
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st) {
   const unsigned items = (unsigned)(a.ntiles * a.segments);
-  if (a.tile_rows == 256) hipLaunchKernelGGL(k_fwd<256>, dim3(items), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(k_fwd<128>, dim3(items), dim3(kThreads), 0, st, a);
+  if (a.tile_rows == 256) hipLaunchKernelGGL(k_fwd<256>, dim3(items), dim3(kFwdThreads), 0, st, a);
+  else hipLaunchKernelGGL(k_fwd<128>, dim3(items), dim3(kFwdThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nblocks = (int)((a.L + 63) / 64);
