@@ -73,6 +73,8 @@ def main():
     ap.add_argument("--chunk-rows", type=int, default=None)
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (scale for HBM byte counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -86,6 +88,16 @@ def main():
 
     import lm_head_chunked_amd as lm
     from lm_head_chunked_amd import _lib, synth
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 copies of {n} bytes (each reads and writes {n >> 10} KiB)")
+        return
 
     _lib.load()
     wl = synth.WORKLOADS[args.workload]

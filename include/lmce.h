@@ -38,8 +38,8 @@
  *     bytes.  Calls that share a workspace must be ordered on one stream.
  *   - Return value: LMCE_OK (0) or a negative lmce_status.  Argument errors
  *     are detected before anything is enqueued.
- *   - Limits: 1 <= L <= 2^24, 1 <= V <= 2^24, 64 <= H <= 16384 with
- *     H % 64 == 0, chunk_rows a multiple of 32 in [32, 1024].
+ *   - Limits: 1 <= L <= 2^21, 1 <= V <= 2^21, 128 <= H <= 16384 with
+ *     H % 128 == 0, chunk_rows a multiple of 32 in [32, 1024].
  */
 #ifndef LMCE_H
 #define LMCE_H
@@ -55,7 +55,7 @@ typedef enum {
   LMCE_OK = 0,
   LMCE_ERR_NULL = -1,        /* a required pointer is NULL or misaligned */
   LMCE_ERR_SHAPE = -2,       /* L, H or V out of range */
-  LMCE_ERR_UNSUPPORTED = -3, /* H % 64 != 0, or chunk_rows not a multiple of 32 in [32, 1024] */
+  LMCE_ERR_UNSUPPORTED = -3, /* H % 128 != 0, chunk_rows not a multiple of 32 in [32, 1024], or the device cannot run the grid */
   LMCE_ERR_WORKSPACE = -4,   /* workspace_bytes smaller than lmce_workspace_size() */
   LMCE_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
   LMCE_ERR_LABEL = -6        /* (asynchronous) a label is outside [0, V) and not ignore_index */

@@ -21,7 +21,7 @@ struct Plan {
   int64_t L, H, V;
   int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
   int64_t Lpad, Vpad;
-  int hs, group_size, xbuf_wgs;
+  int group_size, xbuf_wgs;
   size_t off_zlabel, off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, total;
 };
 
@@ -56,8 +56,7 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->xcd_map = (p->segments == 8 && p->ntiles % 32 == 0) ? 1 : 0;
   p->Lpad = (L + 127) / 128 * 128;
   p->Vpad = (V + 127) / 128 * 128;
-  p->hs = (H % 128 == 0) ? 128 : 64;
-  p->group_size = (int)(H / p->hs);
+  p->group_size = (int)(H / 128);
 
   size_t off = align256(sizeof(WsHeader));
   p->off_zlabel = off;
@@ -105,7 +104,7 @@ extern "C" const char* lmce_strerror(int status) {
     case LMCE_OK: return "ok";
     case LMCE_ERR_NULL: return "a required pointer is NULL or misaligned";
     case LMCE_ERR_SHAPE: return "L, H or V out of range";
-    case LMCE_ERR_UNSUPPORTED: return "unsupported shape: H must be a multiple of 64, chunk_rows a multiple of 32 in [32, 1024]";
+    case LMCE_ERR_UNSUPPORTED: return "unsupported shape: H must be a multiple of 128, chunk_rows a multiple of 32 in [32, 1024]";
     case LMCE_ERR_WORKSPACE: return "workspace smaller than lmce_workspace_size()";
     case LMCE_ERR_HIP: return "HIP runtime error";
     case LMCE_ERR_LABEL: return "a label is outside [0, V) and is not ignore_index";
@@ -207,7 +206,7 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
     const bool dh = pass == 0;
     if (!(which & (dh ? 1 : 2))) continue;
     int resident = 0;
-    if (bwd_resident_wgs(dh, p.hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
+    if (bwd_resident_wgs(dh, &resident) != hipSuccess) return LMCE_ERR_HIP;
     if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
     const int64_t items = dh ? (L + 255) / 256 : (V + 255) / 256;  // row blocks or vocabulary blocks
     int64_t groups = resident / p.group_size;
@@ -215,7 +214,7 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
     if (groups < 1) return LMCE_ERR_UNSUPPORTED;
     a.n_groups = (int)groups;
     if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
-    if (launch_bwd_group(dh, a, p.hs, (int)groups * p.group_size, s) != hipSuccess) return LMCE_ERR_HIP;
+    if (launch_bwd_group(dh, a, (int)groups * p.group_size, s) != hipSuccess) return LMCE_ERR_HIP;
   }
   return LMCE_OK;
 }

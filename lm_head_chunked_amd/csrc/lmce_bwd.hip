@@ -5,18 +5,18 @@
 // G = g/N * valid * (softmax - onehot), dh = G W and dW = G^T h.
 //
 // dh and dW are H wide: a 256 x H fp32 accumulator (4 MiB at H = 4096) does
-// not fit in one compute unit, so each pass runs as groups of s = H / HS
-// workgroups, workgroup j of a group owning an HS-wide slice of the
+// not fit in one compute unit, so each pass runs as groups of s = H / 128
+// workgroups, workgroup j of a group owning a 128-wide slice of the
 // accumulator in registers.  In every round each member recomputes ONE
-// full-H logit tile with MFMA, turns it into bf16 G in registers and writes it
-// to the group's exchange slot; after a group barrier every member
-// contracts all s tiles of the round into its own slice.  Each logit is thus
-// recomputed exactly once per pass and no logit or G tile ever exists for
+// full-H 256 x 256 logit tile with MFMA, turns it into bf16 G in registers
+// and writes it to the group's exchange slot; after a group barrier every
+// member contracts all s tiles of the round into its own slice.  Each logit
+// is thus recomputed exactly once per pass and no logit or G tile exists for
 // more than one round (the exchange holds 2 x s tiles per group).
 //
-//   k_bwd_dh : group = 256 rows of h; rounds sweep the vocabulary, 128 per
+//   k_bwd_dh : group = 256 rows of h; rounds sweep the vocabulary, 256 per
 //              member; dh[rows][slice] += G W   (row-owned, no atomics)
-//   k_bwd_dW : group = 256 vocabulary rows; rounds sweep the tokens, 128 per
+//   k_bwd_dW : group = 256 vocabulary rows; rounds sweep the tokens, 256 per
 //              member; dW[rows][slice] += G^T h (vocabulary-owned, no atomics)
 //
 // The groups run as one cooperative launch (all workgroups resident).  The
@@ -87,20 +87,38 @@ __device__ __forceinline__ bool group_arrive_wait(unsigned* ctr, unsigned target
   return *s_flag != 0;
 }
 
+// Producer and consumer tiles.  Eight waves (two per SIMD) in a 4 x 2 grid:
+// the producer's 256 x 256 logit tile gives each wave 64 x 128 logits (128
+// accumulator registers), the consumer's 256 x 128 accumulator slice 64 x 64
+// (64 registers), which stays live across the rounds of a block.
+constexpr int kBwdThreads = 512;
+constexpr int kSlice = 128;  // H columns owned by one member
+using BwdProducer = TileGemm<256, 256, 4, 2>;
+using BwdConsumer = TileGemm<256, kSlice, 4, 2, kAuxSc1, 1, 1>;
+constexpr int kBwdLds =
+    BwdProducer::LDS_BYTES > BwdConsumer::LDS_BYTES ? BwdProducer::LDS_BYTES : BwdConsumer::LDS_BYTES;
+
+// Byte offset, inside a round's slot, of the 4 consecutive K elements a lane
+// stores: the slot is a sequence of [256][128] bf16 K-tiles; member j fills
+// K-tiles 2j and 2j+1 (its 256 K indices), `row` is the tile row (M of the
+// consumer) and `kin` the K index inside the member's 256 (a multiple of 8;
+// the lane half adds 4 through the vector offset).
+__device__ __forceinline__ uint32_t slot_offset(int j, int row, int kin) {
+  return (uint32_t)(((((j << 1) + (kin >> 7)) * 256 + row) * 128 + (kin & 127)) * 2);
+}
+
 // ---------------------------------------------------------------- dh pass
-// Group = 256 rows.  Round k: member j recomputes the logit tile of
-// vocabulary rows [(k*s + j)*128, +128) against the group's rows (A = W,
+// Group = 256 rows of h.  Round k: member j recomputes the logit tile of
+// vocabulary rows [(k*s + j)*256, +256) against the group's rows (A = W,
 // B = h, so the tile is z^T: vocabulary on M, tokens on N), forms
-// G[token][v] and stores it into columns [j*128, +128) of the round's slot
-// [256 tokens][s*128].  Then every member accumulates
-//   dh[rows][c0 .. c0+HS] += slot[256][K] * W^T[c0 .. c0+HS][round's vocabulary]
-// with K = 128 * (tiles in the round).
-template <int HS>
-__global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
-  using P = TileGemm<128, 256, 2, 2>;    // producer: 128 vocabulary x 256 tokens
-  using C = TileGemm<256, HS, 2, 2, kAuxSc1, 1, 1>;  // consumer: 256 tokens x HS columns, K-tiled operands
-  constexpr int LDS = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
+// G[token][v] and stores it as the member's two K-tiles of the round's slot
+// [256 tokens][K].  Then every member accumulates
+//   dh[rows][c0 .. c0+128] += slot[256][K] * W^T[c0 .. c0+128][round's vocabulary]
+// with K = 128 * (K-tiles in the round).
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
+  using P = BwdProducer;
+  using C = BwdConsumer;
+  __shared__ __attribute__((aligned(16))) char lds[kBwdLds];
   __shared__ int s_flag;
 
   const int s = p.group_size;
@@ -110,12 +128,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
   const int wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t H = p.H, V = p.V, L = p.L;
-  const int64_t c0 = (int64_t)j * HS;
-  const int64_t slot_elems = (int64_t)s * 256 * 128;  // slot = s tiles of [256][128]
-  // per-lane part of an exchange store: row lane%32, 4 columns per lane half
+  const int64_t c0 = (int64_t)j * kSlice;
+  const int64_t slot_elems = (int64_t)s * 256 * 256;  // 2s K-tiles of [256][128]
+  // per-lane part of an exchange store: tile row lane%32, 4 K elements per lane half
   const uint32_t xvoff = (uint32_t)(((lane & 31) * 128 + ((lane >> 5) << 2)) * 2);
+  const int vt256 = (int)((V + 255) / 256);
   const int vt128 = (int)((V + 127) / 128);
-  const int rounds = (vt128 + s - 1) / s;
+  const int rounds = (vt256 + s - 1) / s;
   const int nrb = (int)((L + 255) / 256);
   const int n_valid = p.hdr->n_valid;
   const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
@@ -124,15 +143,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
   for (int rb = g; rb < nrb; rb += p.n_groups) {
     const int64_t r0 = (int64_t)rb * 256;
     const int64_t rend = min(r0 + 256, L);
-    // producer wave (wm: vocabulary half, wn: token half); lane's 4 tokens
+    // producer wave (wm: vocabulary quarter, wn: token half); lane's 4 tokens
     float lse2[4], scale[4];
-    int64_t lab[4];
+    int lab[4];  // label, or -2^30 for rows that take no gradient
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int64_t t = r0 + wn * 128 + nb * 32 + (lane & 31);
       const int64_t y = t < rend ? p.labels[t] : p.ignore_index;
       const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
-      lab[nb] = valid ? y : INT64_MIN / 2;
+      lab[nb] = valid ? (int)y : -(1 << 30);
       scale[nb] = valid ? gscale : 0.f;
       lse2[nb] = t < rend ? p.lse[t] * kLog2e : INFINITY;  // rows past L: probability 0
     }
@@ -144,20 +163,19 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
       u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
       const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
       const int vt = k * s + j;
-      if (vt < vt128) {
-        const int64_t v0 = (int64_t)vt * 128;
+      if (vt < vt256) {
+        const int v0 = vt * 256;
         f32x16 z[P::MB][P::NB];
         zero_acc(z);
-        P::run(linear_operand(p.W + v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2)), oh, (int)H, lds, z);
+        P::run(linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2)), oh, (int)H, lds,
+               z);
         // G[token][v] = scale * (exp(z - lse) - [v == y]); 4 consecutive v per store.
-        // Tile-local 32-bit coordinates: vl = v - v0, label at lab - v0.
-        const int vlim = (int)min<int64_t>(V - v0, 128);
+        // Tile-local coordinates: vl = v - v0, the label at lab - v0.
+        const int vlim = min((int)(V - v0), 256);
         const int jo = opaque_s(j);  // keeps the store offsets below from being hoisted out of the loop
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const int tl = wn * 128 + nb * 32 + (lane & 31);
-          const int64_t dl = lab[nb] - v0;
-          const int yl = (dl >= 0 && dl < 128) ? (int)dl : -1;
+          const int yl = lab[nb] - v0;  // outside [0, 256) if the label is not in this tile
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -170,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
                 pr = (vl0 + e == yl) ? pr - 1.f : pr;
                 gv[e] = pr * ((vl0 + e < vlim) ? scale[nb] : 0.f);
               }
-              const uint32_t soff = (uint32_t)((((int64_t)jo * 256 + wn * 128 + nb * 32) * 128 + wm * 64 + mb * 32 + qq * 8) * 2);
+              const uint32_t soff = slot_offset(jo, wn * 128 + nb * 32, wm * 64 + mb * 32 + qq * 8);
               store_sc1_b64(rslot, xvoff, soff, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
             }
           __builtin_amdgcn_sched_barrier(0);
@@ -178,33 +196,31 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(BwdArgs p) {
       }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
         return;
-      const int ntl = min(s, vt128 - k * s);
-      const int64_t vbase = (int64_t)k * s * 128;
-      // A: the slot's tiles [256][128] (K-tiled); B: W^T tiles [H][128] of the
-      // round's vocabulary, rows c0 .. c0+HS (K-tiled)
+      const int ntl = min(2 * s, vt128 - k * 2 * s);
+      const int64_t vbase = (int64_t)k * s * 256;
+      // A: the slot's K-tiles [256][128]; B: W^T tiles [H][128] of the round's
+      // vocabulary, rows c0 .. c0+128 (K-tiled)
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
              tiled_operand(p.WT + (vbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
              lds, dacc);
     }
-    // dh[r][c] for r < L (waves: wm token half, wn column half)
-    store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 128, wn * (HS / 2), lane);
+    // dh[r][c] for r < L (waves: wm token quarter, wn column half)
+    store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * 64, lane);
   }
 }
 
 // ---------------------------------------------------------------- dW pass
 // Group = 256 vocabulary rows.  Round k: member j recomputes the logit tile
-// of tokens [(k*s + j)*128, +128) against the group's vocabulary rows (A = h,
-// B = W: tokens on M, vocabulary on N), forms G^T[v][token] and stores it
-// into columns [j*128, +128) of the round's slot [256 v][s*128].  Then
-//   dW[v rows][c0 .. c0+HS] += slot[256][K] * h^T[c0 .. c0+HS][round's tokens].
-template <int HS>
-__global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
-  using P = TileGemm<128, 256, 2, 2>;    // producer: 128 tokens x 256 vocabulary
-  using C = TileGemm<256, HS, 2, 2, kAuxSc1, 1, 1>;  // consumer: 256 vocabulary x HS columns, K-tiled operands
-  constexpr int LDS = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
-  __shared__ float row_lse2[128], row_scale[128];
-  __shared__ int row_lab[128];  // label - v0 of the group's vocabulary block, or -1
+// of tokens [(k*s + j)*256, +256) against the group's vocabulary rows (A = h,
+// B = W: tokens on M, vocabulary on N), forms G^T[v][token] and stores it as
+// the member's two K-tiles of the round's slot [256 v][K].  Then
+//   dW[v rows][c0 .. c0+128] += slot[256][K] * h^T[c0 .. c0+128][round's tokens].
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
+  using P = BwdProducer;
+  using C = BwdConsumer;
+  __shared__ __attribute__((aligned(16))) char lds[kBwdLds];
+  __shared__ float row_lse2[256], row_scale[256];
+  __shared__ int row_lab[256];  // label - v0 of the group's vocabulary block, or -1
   __shared__ int s_flag;
 
   const int s = p.group_size;
@@ -214,11 +230,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
   const int wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t H = p.H, V = p.V, L = p.L;
-  const int64_t c0 = (int64_t)j * HS;
-  const int64_t slot_elems = (int64_t)s * 256 * 128;
+  const int64_t c0 = (int64_t)j * kSlice;
+  const int64_t slot_elems = (int64_t)s * 256 * 256;
   const uint32_t xvoff = (uint32_t)(((lane & 31) * 128 + ((lane >> 5) << 2)) * 2);
+  const int rt256 = (int)((L + 255) / 256);
   const int rt128 = (int)((L + 127) / 128);
-  const int rounds = (rt128 + s - 1) / s;
+  const int rounds = (rt256 + s - 1) / s;
   const int nvb = (int)((V + 255) / 256);
   const int n_valid = p.hdr->n_valid;
   const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
@@ -233,10 +250,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
       u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
       const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
       const int rt = k * s + j;
-      if (rt < rt128) {
-        const int64_t r0 = (int64_t)rt * 128;
-        const int64_t rend = min(r0 + 128, L);
-        if (threadIdx.x < 128) {
+      if (rt < rt256) {
+        const int64_t r0 = (int64_t)rt * 256;
+        const int64_t rend = min(r0 + 256, L);
+        if (threadIdx.x < 256) {
           const int64_t t = r0 + threadIdx.x;
           const int64_t y = t < rend ? p.labels[t] : p.ignore_index;
           const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
@@ -279,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
                 pr = (vl == tlab[e]) ? pr - 1.f : pr;
                 gv[e] = pr * (tsc[e] * vmask[nb]);
               }
-              const uint32_t soff = (uint32_t)((((int64_t)jo * 256 + wn * 128 + nb * 32) * 128 + wm * 64 + mb * 32 + qq * 8) * 2);
+              const uint32_t soff = slot_offset(jo, wn * 128 + nb * 32, wm * 64 + mb * 32 + qq * 8);
               store_sc1_b64(rslot, xvoff, soff, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -287,13 +304,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dW(BwdArgs p) {
       }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
         return;
-      const int ntl = min(s, rt128 - k * s);
-      const int64_t rbase = (int64_t)k * s * 128;
+      const int ntl = min(2 * s, rt128 - k * 2 * s);
+      const int64_t rbase = (int64_t)k * s * 256;
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
              tiled_operand(p.hT + (rbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
              lds, dacc);
     }
-    store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, dacc, wm * 128, wn * (HS / 2), lane);
+    store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, dacc, wm * 64, wn * 64, lane);
   }
 }
 
@@ -310,21 +327,11 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
-namespace {
-
-template <int HS>
-const void* pick_kernel(bool dh) {
-  return dh ? reinterpret_cast<const void*>(&k_bwd_dh<HS>) : reinterpret_cast<const void*>(&k_bwd_dW<HS>);
+const void* bwd_kernel(bool dh) {
+  return dh ? reinterpret_cast<const void*>(&k_bwd_dh) : reinterpret_cast<const void*>(&k_bwd_dW);
 }
 
-const void* bwd_kernel(bool dh, int hs) {
-  if (hs == 128) return pick_kernel<128>(dh);
-  return pick_kernel<64>(dh);
-}
-
-}  // namespace
-
-hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs) {
+hipError_t bwd_resident_wgs(bool dh, int* wgs) {
   int dev = 0, cus = 0, per = 0, coop = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -333,16 +340,16 @@ hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs) {
   e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
   if (e != hipSuccess) return e;
   if (!coop) return hipErrorNotSupported;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_kernel(dh, hs), kThreads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_kernel(dh), kBwdThreads, 0);
   if (e != hipSuccess) return e;
   *wgs = cus * per;
   return hipSuccess;
 }
 
-hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int hs, int n_wgs, hipStream_t st) {
+hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int n_wgs, hipStream_t st) {
   BwdArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchCooperativeKernel(bwd_kernel(dh, hs), dim3((unsigned)n_wgs), dim3(kThreads), args, 0, st);
+  return hipLaunchCooperativeKernel(bwd_kernel(dh), dim3((unsigned)n_wgs), dim3(kBwdThreads), args, 0, st);
 }
 
 }  // namespace lmce

@@ -9,11 +9,11 @@ namespace lmce {
 
 constexpr int kStatusLabel = 1;     // asynchronous flag: a label was out of range
 constexpr int kStatusSync = 2;      // asynchronous flag: a group wait timed out
-constexpr int kStageK = 64;         // hidden-size granularity
+constexpr int kStageK = 128;        // hidden-size granularity (the backward slices H by 128)
 constexpr int kVTile = 256;         // vocabulary rows per forward logit tile
 constexpr int kSyncStride = 64;     // u32 words between two groups' counters (256 bytes)
 constexpr int kMaxBwdWGs = 256;     // upper bound of a backward cooperative grid
-constexpr int kXbufPerWG = 2 * 256 * 128 * 2;  // exchange bytes per backward workgroup
+constexpr int kXbufPerWG = 2 * 256 * 256 * 2;  // exchange bytes per backward workgroup (2 slots x one 256 x 256 bf16 tile)
 
 // First 256 bytes of the workspace.
 struct WsHeader {
@@ -51,11 +51,11 @@ struct BwdArgs {
   const uint16_t* hT;   // h transposed tile-major: [Lpad/128][H][128], zero past L
   const uint16_t* WT;   // W transposed tile-major: [Vpad/128][H][128], zero past V
   int64_t L, H, V, ignore_index, Lpad, Vpad;
-  int group_size;       // workgroups per group = H / HS
+  int group_size;       // workgroups per group = H / 128
   int n_groups;
   int spin_limit;       // bound of every group wait
   unsigned* sync;       // [n_groups * kSyncStride] arrival counters, zeroed before the launch
-  uint16_t* xbuf;       // [n_groups][2][group_size][256][128] exchange slots
+  uint16_t* xbuf;       // [n_groups][2][2 * group_size][256][128] exchange slots
   WsHeader* hdr;
   float* dh;
   float* dW;
@@ -66,7 +66,7 @@ hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int6
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
 hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
-hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs);
-hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int hs, int n_wgs, hipStream_t st);
+hipError_t bwd_resident_wgs(bool dh, int* wgs);
+hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int n_wgs, hipStream_t st);
 
 }  // namespace lmce

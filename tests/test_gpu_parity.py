@@ -78,12 +78,13 @@ def test_tiny_workload_parity():
 
 
 RAGGED = [
-    (300, 64, 700, 0.2),
-    (129, 192, 257, 0.0),
-    (1, 64, 1, 0.0),
+    (300, 128, 700, 0.2),
+    (129, 256, 257, 0.0),
+    (1, 128, 1, 0.0),
     (77, 128, 4097, 0.5),
-    (256, 320, 1000, 0.1),
+    (256, 384, 1000, 0.1),
     (1000, 512, 130, 0.05),
+    (513, 640, 2000, 0.3),
 ]
 
 
@@ -137,7 +138,7 @@ def test_zero_weights_give_ln_V():
 
 def test_all_rows_ignored():
     say("[case] N_valid = 0")
-    h, W, y = synth.random_case(130, 64, 500, seed=4)
+    h, W, y = synth.random_case(130, 128, 500, seed=4)
     y[:] = -100
     gpu = run_gpu(h, W, y)
     assert math.isnan(gpu["loss"])
@@ -147,7 +148,7 @@ def test_all_rows_ignored():
 
 def test_out_of_range_label_is_reported():
     say("[case] bad label")
-    h, W, y = synth.random_case(64, 64, 100, seed=6, ignore_frac=0.0)
+    h, W, y = synth.random_case(64, 128, 100, seed=6, ignore_frac=0.0)
     y[10] = 100
     gpu = run_gpu(h, W, y)
     assert gpu["status"] == _lib.LMCE_ERR_LABEL
