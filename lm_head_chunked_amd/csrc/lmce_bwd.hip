@@ -94,17 +94,37 @@ __device__ __forceinline__ bool group_arrive_wait(unsigned* ctr, unsigned target
 constexpr int kBwdThreads = 512;
 constexpr int kSlice = 128;  // H columns owned by one member
 using BwdProducer = TileGemm<256, 256, 4, 2>;
-using BwdConsumer = TileGemm<256, kSlice, 4, 2, kAuxSc1, 1, 1>;
+using BwdConsumer = TileGemm<256, kSlice, 4, 2, kAuxSc1, 1, 1, true>;
 constexpr int kBwdLds =
     BwdProducer::LDS_BYTES > BwdConsumer::LDS_BYTES ? BwdProducer::LDS_BYTES : BwdConsumer::LDS_BYTES;
 
-// Byte offset, inside a round's slot, of the 4 consecutive K elements a lane
-// stores: the slot is a sequence of [256][128] bf16 K-tiles; member j fills
-// K-tiles 2j and 2j+1 (its 256 K indices), `row` is the tile row (M of the
-// consumer) and `kin` the K index inside the member's 256 (a multiple of 8;
-// the lane half adds 4 through the vector offset).
-__device__ __forceinline__ uint32_t slot_offset(int j, int row, int kin) {
-  return (uint32_t)(((((j << 1) + (kin >> 7)) * 256 + row) * 128 + (kin & 127)) * 2);
+// A member's G tile is staged in LDS as [256 rows][256 K] bf16 (512 bytes
+// per row), the 16-byte chunk c of row r at chunk c ^ (r % 32): 32 lanes that
+// write the same chunk of 32 consecutive rows, or read the 32 chunks of one
+// row, hit distinct banks.  Byte offset of K elements k .. k+3 (k % 4 == 0).
+__device__ __forceinline__ uint32_t gstage_offset(int row, int k) {
+  return (uint32_t)(row * 512 + ((((k >> 3) ^ (row & 31)) << 4) | ((k & 4) << 1)));
+}
+
+__device__ __forceinline__ void gstage_put(char* lds, int row, int k, uint64_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) uint64_t*>(
+      (__attribute__((address_space(3))) char*)lds + gstage_offset(row, k)) = v;
+}
+
+// Copies the staged tile into the member's two K-tiles (2j, 2j+1) of the
+// round's slot, a sequence of [256][128] bf16 K-tiles: each half-wave writes
+// one 256-byte row segment per instruction.
+__device__ __forceinline__ void gstage_flush(const char* lds, rsrc_t rslot, int j) {
+  const int t = threadIdx.x;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int idx = i * 512 + t;   // 16-byte chunk of the tile
+    const int row = idx >> 5, c = idx & 31;
+    const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+        (const __attribute__((address_space(3))) char*)lds + row * 512 + ((c ^ (row & 31)) << 4));
+    const uint32_t voff = (uint32_t)(((c >> 4) * 256 * 128 + row * 128 + (c & 15) * 8) * 2);
+    store_sc1_b128(rslot, voff, (uint32_t)j * 2u * 256u * 128u * 2u, v);
+  }
 }
 
 // ---------------------------------------------------------------- dh pass
@@ -130,8 +150,6 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   const int64_t H = p.H, V = p.V, L = p.L;
   const int64_t c0 = (int64_t)j * kSlice;
   const int64_t slot_elems = (int64_t)s * 256 * 256;  // 2s K-tiles of [256][128]
-  // per-lane part of an exchange store: tile row lane%32, 4 K elements per lane half
-  const uint32_t xvoff = (uint32_t)(((lane & 31) * 128 + ((lane >> 5) << 2)) * 2);
   const int vt256 = (int)((V + 255) / 256);
   const int vt128 = (int)((V + 127) / 128);
   const int rounds = (vt256 + s - 1) / s;
@@ -169,10 +187,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
         zero_acc(z);
         P::run(linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2)), oh, (int)H, lds,
                z);
-        // G[token][v] = scale * (exp(z - lse) - [v == y]); 4 consecutive v per store.
-        // Tile-local coordinates: vl = v - v0, the label at lab - v0.
+        // G[token][v] = scale * (exp(z - lse) - [v == y]), staged in LDS as
+        // [token][v], 4 consecutive v per write.  Tile-local coordinates:
+        // vl = v - v0, the label at lab - v0.
         const int vlim = min((int)(V - v0), 256);
-        const int jo = opaque_s(j);  // keeps the store offsets below from being hoisted out of the loop
+        raw_barrier();  // every wave is done with the GEMM's last LDS stage
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int yl = lab[nb] - v0;  // outside [0, 256) if the label is not in this tile
@@ -188,11 +207,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
                 pr = (vl0 + e == yl) ? pr - 1.f : pr;
                 gv[e] = pr * ((vl0 + e < vlim) ? scale[nb] : 0.f);
               }
-              const uint32_t soff = slot_offset(jo, wn * 128 + nb * 32, wm * 64 + mb * 32 + qq * 8);
-              store_sc1_b64(rslot, xvoff, soff, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
+              gstage_put(lds, wn * 128 + nb * 32 + (lane & 31), vl0, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
             }
           __builtin_amdgcn_sched_barrier(0);
         }
+        __syncthreads();
+        gstage_flush(lds, rslot, j);
       }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
         return;
@@ -232,7 +252,6 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   const int64_t H = p.H, V = p.V, L = p.L;
   const int64_t c0 = (int64_t)j * kSlice;
   const int64_t slot_elems = (int64_t)s * 256 * 256;
-  const uint32_t xvoff = (uint32_t)(((lane & 31) * 128 + ((lane >> 5) << 2)) * 2);
   const int rt256 = (int)((L + 255) / 256);
   const int rt128 = (int)((L + 127) / 128);
   const int rounds = (rt256 + s - 1) / s;
@@ -269,7 +288,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
         // Token data is read once per 4-token group and reused for the
         // lane's 4 vocabulary columns; columns past V get a zero factor.
         const int vlim = (int)min<int64_t>(V - v0, 256);
-        const int jo = opaque_s(j);  // keeps the store offsets below from being hoisted out of the loop
+        raw_barrier();  // every wave is done with the GEMM's last LDS stage
         float vmask[4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) vmask[nb] = (wn * 128 + nb * 32 + (lane & 31) < vlim) ? 1.f : 0.f;
@@ -296,11 +315,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
                 pr = (vl == tlab[e]) ? pr - 1.f : pr;
                 gv[e] = pr * (tsc[e] * vmask[nb]);
               }
-              const uint32_t soff = slot_offset(jo, wn * 128 + nb * 32, wm * 64 + mb * 32 + qq * 8);
-              store_sc1_b64(rslot, xvoff, soff, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
+              gstage_put(lds, vl, tl0, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
             }
             __builtin_amdgcn_sched_barrier(0);
           }
+        __syncthreads();
+        gstage_flush(lds, rslot, j);
       }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
         return;

@@ -122,6 +122,22 @@ __device__ __forceinline__ bf16x8 stage_frag(const char* region, int row, int ch
   return v;
 }
 
+// Waits until at most N LDS reads of this wave are outstanding (reads
+// complete in order, so the fragments issued before the last N are ready).
+// The fragments are tied to the wait so that no instruction using them is
+// scheduled before it.
+template <int N, int MB, int NB>
+__device__ __forceinline__ void lds_wait_frags_n(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
+  if constexpr (MB == 2 && NB == 4)
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]), "+v"(fb[3])
+                 : "n"(N));
+  else if constexpr (MB == 2 && NB == 2)
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]), "+v"(fb[1]) : "n"(N));
+  else
+    static_assert(MB == 0, "unsupported fragment count");
+}
+
 // Waits for every outstanding LDS read of this wave.  The fragments are
 // tied to the wait so that no instruction using them is scheduled before it.
 template <int MB, int NB>
@@ -168,7 +184,7 @@ __device__ __forceinline__ uint32_t k_offset(const Operand& o, int kt) {
   else return (uint32_t)(kt >> 2) * o.tstride + (uint32_t)(kt & 3) * 64u;
 }
 
-template <int BM, int BN, int WM, int WN, int AUXA = 0, int KTA = 0, int KTB = 0>
+template <int BM, int BN, int WM, int WN, int AUXA = 0, int KTA = 0, int KTB = 0, bool PF = false>
 struct TileGemm {
   static constexpr int NW = WM * WN;             // waves
   static constexpr int NT = 64 * NW;             // threads
@@ -193,9 +209,11 @@ struct TileGemm {
     const int wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
     const int nk = K / BK;
-    // Every earlier reader of this LDS is past this barrier, and no earlier
-    // vector memory operation of this wave is still counted in vmcnt.
+    // Every earlier reader of this LDS is past this barrier, every earlier
+    // LDS write of the workgroup has landed, and no earlier vector memory
+    // operation of this wave is still counted in vmcnt.
     wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     raw_barrier();
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
@@ -209,19 +227,44 @@ struct TileGemm {
       if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, a, b, lds, wave, lane);
       const char* sa = lds + (kt % STAGES) * STAGE_BYTES;
       const char* sb = sa + BM * 64;
+      if constexpr (PF) {
+        // both 16-wide K sub-steps' fragments up front: the second half's
+        // reads complete while the first half's MFMAs run
+        bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
+        const int ca = lane >> 5, cb = 2 + (lane >> 5);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c = 2 * ks + (lane >> 5);
-        bf16x8 fa[MB], fb[NB];
+        for (int mb = 0; mb < MB; ++mb) fa0[mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), ca);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) fa[mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), c);
+        for (int nb = 0; nb < NB; ++nb) fb0[nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), ca);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fb[nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), c);
-        lds_wait_frags(fa, fb);
+        for (int mb = 0; mb < MB; ++mb) fa1[mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), cb);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) fb1[nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), cb);
+        lds_wait_frags_n<MB + NB>(fa0, fb0);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa[mb], fb[nb], acc[mb][nb]);
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa0[mb], fb0[nb], acc[mb][nb]);
+        lds_wait_frags_n<0>(fa1, fb1);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa1[mb], fb1[nb], acc[mb][nb]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int c = 2 * ks + (lane >> 5);
+          bf16x8 fa[MB], fb[NB];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) fa[mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), c);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) fb[nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), c);
+          lds_wait_frags(fa, fb);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa[mb], fb[nb], acc[mb][nb]);
+        }
       }
     }
   }
@@ -272,6 +315,11 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // soff wave-uniform (kept in a scalar register).
 __device__ __forceinline__ void store_sc1_b64(rsrc_t rs, uint32_t voff, uint32_t soff, uint64_t v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, voff, soff, kAuxSc1);
+}
+
+// 16-byte buffer store, coherent at device scope.
+__device__ __forceinline__ void store_sc1_b128(rsrc_t rs, uint32_t voff, uint32_t soff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, soff, kAuxSc1);
 }
 
 // 4-byte buffer store (stores past the resource end are dropped).

@@ -103,7 +103,7 @@ constexpr int kFwdWM = 4, kFwdWN = 2, kFwdThreads = 64 * kFwdWM * kFwdWN;
 
 template <int BN>
 __global__ __launch_bounds__(kFwdThreads) void k_fwd(FwdArgs p) {
-  using G = TileGemm<256, BN, kFwdWM, kFwdWN>;
+  using G = TileGemm<256, BN, kFwdWM, kFwdWN, 0, 0, 0, true>;
   constexpr int MB = G::MB, NB = G::NB;
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
   __shared__ float red_m[kFwdWM - 1][BN], red_s[kFwdWM - 1][BN];
