@@ -23,8 +23,11 @@ Flop accounting (algorithmic, independent of the schedule):
 """
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -40,6 +43,30 @@ PEAK_HBM_GBS = 8000.0
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    """sha256 over the HIP sources (file names and contents, sorted by name)."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "lm_head_chunked_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, kernel):
+    """HBM-side bytes per launch of `kernel`, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload; None if there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256: ([0-9a-f]{64})", text)
+    if m is None or m.group(1) != kernel_source_digest():
+        return None
+    m = re.search(rf"^{re.escape(kernel)} hbm_bytes_per_launch: (\d+)$", text, re.M)
+    return int(m.group(1)) if m else None
 
 
 def cpu_baseline(wl, W_cpu, h_rows, y_rows):
@@ -193,7 +220,7 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": dom_kernel, "call": dom, "achieved": dom_tflops,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None, "mean_ms": calls[dom][1],
+            "traffic": recorded_traffic(wl.name, dom_kernel), "mean_ms": calls[dom][1],
         },
         "cpu_baseline": None,
     }

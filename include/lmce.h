@@ -68,8 +68,10 @@ int lmce_version(void);
 const char* lmce_strerror(int status);
 
 /*
- * Bytes of device workspace that lmce_fwd / lmce_bwd need for this shape.
- * The size is O(L * segments + V * H-independent terms): it never holds an
+ * Bytes of device workspace that lmce_fwd / lmce_bwd need for this shape:
+ * transposed bf16 copies of h and W for the backward ((L + V) * H * 2 bytes,
+ * rounded up to 128 rows), per-row forward partials (O(L) floats), and a
+ * fixed exchange ring for the backward (at most 64 MiB).  It never holds an
  * L x V array.  Writes the size to *bytes.  Returns LMCE_OK or a shape error.
  */
 int lmce_workspace_size(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, size_t* bytes);
@@ -100,9 +102,13 @@ int lmce_fwd(const void* h, const void* W, const int64_t* labels,
 /*
  * Backward.  Same page and sections; the gradient of the mean NLL is
  * G = g/N * valid * (softmax - onehot).  Each logit tile is recomputed from
- * h and W, turned into G in registers and contracted at once into
+ * h and W, turned into bf16 G and contracted in the same round into
  *   dh_out fp32 [L, H] = G W     (overwritten, not accumulated)
  *   dW_out fp32 [V, H] = G^T h   (overwritten, not accumulated)
+ * by the co-resident workgroups that own the 128-wide H slices of the
+ * outputs; a G tile lives only in the workspace's exchange ring for the one
+ * round that consumes it.  The device must support cooperative launches
+ * (otherwise LMCE_ERR_HIP or LMCE_ERR_UNSUPPORTED).
  *
  *   lse        fp32 [L]  the lse_out of lmce_fwd on the same inputs
  *   grad_loss  fp32 [1]  device scalar g, the upstream gradient of the loss
@@ -130,8 +136,10 @@ int lmce_bwd_dW(const void* h, const void* W, const int64_t* labels, const float
 
 /*
  * Synchronises `stream` and returns the asynchronous status recorded in the
- * workspace by the last lmce_fwd / lmce_bwd on it: LMCE_OK or LMCE_ERR_LABEL
- * (or LMCE_ERR_HIP if the synchronisation itself failed).
+ * workspace by the last lmce_fwd / lmce_bwd on it: LMCE_OK, LMCE_ERR_LABEL,
+ * or LMCE_ERR_HIP if the synchronisation failed or a backward workgroup
+ * gave up waiting for the other members of its group (a bounded wait; the
+ * gradients are then incomplete).
  */
 int lmce_read_status(const void* workspace, void* stream);
 

@@ -22,7 +22,7 @@ struct Plan {
   int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
   int64_t Lpad, Vpad;
   int group_size, xbuf_wgs;
-  size_t off_zlabel, off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, total;
+  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -59,8 +59,6 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->group_size = (int)(H / 128);
 
   size_t off = align256(sizeof(WsHeader));
-  p->off_zlabel = off;
-  off = align256(off + sizeof(float) * (size_t)L);
   p->off_pm = off;
   off = align256(off + sizeof(float) * (size_t)L * (size_t)p->segments);
   p->off_ps = off;
@@ -152,7 +150,6 @@ extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int
   a.vtiles_per_seg = p.vtiles_per_seg;
   a.xcd_map = p.xcd_map;
   a.hdr = hdr;
-  a.zlabel = at<float>(workspace, p.off_zlabel);
   a.part_m = at<float>(workspace, p.off_pm);
   a.part_s = at<float>(workspace, p.off_ps);
   a.block_sum = at<float>(workspace, p.off_bsum);

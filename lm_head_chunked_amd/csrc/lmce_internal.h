@@ -36,7 +36,6 @@ struct FwdArgs {
   int vtiles_per_seg;   // vocabulary tiles per segment
   int xcd_map;          // 1: XCD-aware item order (8 segments, ntiles % 32 == 0)
   WsHeader* hdr;
-  float* zlabel;        // (unused) reserved
   float* part_m;        // [segments][L] running max per row and segment
   float* part_s;        // [segments][L] sum of exp(z - max) per row and segment
   float* block_sum;     // [ceil(L/64)] per-block nll sums
