@@ -21,8 +21,8 @@ struct Plan {
   int64_t L, H, V;
   int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
   int64_t Lpad, Vpad;
-  int group_size, xbuf_wgs;
-  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, total;
+  int hs, group_size, xbuf_wgs;
+  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -56,7 +56,8 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->xcd_map = (p->segments == 8 && p->ntiles % 32 == 0) ? 1 : 0;
   p->Lpad = (L + 127) / 128 * 128;
   p->Vpad = (V + 127) / 128 * 128;
-  p->group_size = (int)(H / 128);
+  p->hs = (H % 256 == 0) ? 256 : 128;  // H slice of one backward workgroup
+  p->group_size = (int)(H / p->hs);
 
   size_t off = align256(sizeof(WsHeader));
   p->off_pm = off;
@@ -79,6 +80,8 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   if (wgs > kMaxBwdWGs) wgs = kMaxBwdWGs;
   p->xbuf_wgs = (int)wgs;
   off = align256(off + (size_t)wgs * kXbufPerWG);
+  p->off_park = off;
+  if (p->hs == 256) off = align256(off + (size_t)wgs * kParkPerWG);
   p->total = off;
   return LMCE_OK;
 }
@@ -196,6 +199,7 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
   a.spin_limit = kSpinLimit;
   a.sync = at<unsigned>(workspace, p.off_sync);
   a.xbuf = at<uint16_t>(workspace, p.off_xbuf);
+  a.park = at<float>(workspace, p.off_park);
   a.hdr = hdr;
   a.dh = dh_out;
   a.dW = dW_out;
@@ -203,7 +207,7 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
     const bool dh = pass == 0;
     if (!(which & (dh ? 1 : 2))) continue;
     int resident = 0;
-    if (bwd_resident_wgs(dh, &resident) != hipSuccess) return LMCE_ERR_HIP;
+    if (bwd_resident_wgs(dh, p.hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
     if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
     const int64_t items = dh ? (L + 255) / 256 : (V + 255) / 256;  // row blocks or vocabulary blocks
     int64_t groups = resident / p.group_size;
@@ -211,7 +215,7 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
     if (groups < 1) return LMCE_ERR_UNSUPPORTED;
     a.n_groups = (int)groups;
     if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
-    if (launch_bwd_group(dh, a, (int)groups * p.group_size, s) != hipSuccess) return LMCE_ERR_HIP;
+    if (launch_bwd_group(dh, a, p.hs, (int)groups * p.group_size, s) != hipSuccess) return LMCE_ERR_HIP;
   }
   return LMCE_OK;
 }

@@ -87,16 +87,58 @@ __device__ __forceinline__ bool group_arrive_wait(unsigned* ctr, unsigned target
   return *s_flag != 0;
 }
 
-// Producer and consumer tiles.  Eight waves (two per SIMD) in a 4 x 2 grid:
+// Producer and consumer tiles.  Eight waves (two per SIMD) in a 4 x 2 grid;
 // the producer's 256 x 256 logit tile gives each wave 64 x 128 logits (128
-// accumulator registers), the consumer's 256 x 128 accumulator slice 64 x 64
-// (64 registers), which stays live across the rounds of a block.
+// accumulator registers).  HS is the H slice one member owns:
+//   HS = 128: the 256 x 128 accumulator slice (64 registers per lane) stays
+//             in registers across the rounds of a block, beside the logit tile;
+//   HS = 256: the 256 x 256 slice (128 registers) does not fit beside the
+//             logit tile, so between two contractions it is parked in the
+//             workgroup's own workspace area (256 KiB out and back per round)
+//             and both GEMMs run on square 256 x 256 tiles.
 constexpr int kBwdThreads = 512;
-constexpr int kSlice = 128;  // H columns owned by one member
-using BwdProducer = TileGemm<256, 256, 4, 2>;
-using BwdConsumer = TileGemm<256, kSlice, 4, 2, kAuxSc1, 1, 1, true>;
-constexpr int kBwdLds =
-    BwdProducer::LDS_BYTES > BwdConsumer::LDS_BYTES ? BwdProducer::LDS_BYTES : BwdConsumer::LDS_BYTES;
+
+template <int HS>
+struct BwdCfg {
+  static constexpr bool kPark = HS == 256;
+  using P = TileGemm<256, 256, 4, 2, 0, 0, 0, kPark>;
+  using C = TileGemm<256, HS, 4, 2, kAuxSc1, 1, 1, true>;
+  static constexpr int kLds = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
+};
+
+// Parking area of one workgroup: for each wave, each 16-byte group q of a
+// lane's accumulator registers is one contiguous KiB (lane-major inside), so
+// every transfer instruction moves a whole KiB.  Plain global accesses: the
+// same lane reads back what it wrote.
+template <int MB, int NB>
+__device__ __forceinline__ void park_acc(const f32x16 (&acc)[MB][NB], float* area, int wave, int lane) {
+  float4* dst = reinterpret_cast<float4*>(area) + wave * MB * NB * 4 * 64 + lane;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dst[((mb * NB + nb) * 4 + q) * 64] =
+            make_float4(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
+}
+
+template <int MB, int NB>
+__device__ __forceinline__ void unpark_acc(f32x16 (&acc)[MB][NB], const float* area, int wave, int lane) {
+  const float4* src = reinterpret_cast<const float4*>(area) + wave * MB * NB * 4 * 64 + lane;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = src[((mb * NB + nb) * 4 + q) * 64];
+        acc[mb][nb][4 * q] = v.x;
+        acc[mb][nb][4 * q + 1] = v.y;
+        acc[mb][nb][4 * q + 2] = v.z;
+        acc[mb][nb][4 * q + 3] = v.w;
+      }
+}
 
 // A member's G tile is staged in LDS as [256 rows][256 K] bf16 (512 bytes
 // per row), the 16-byte chunk c of row r at chunk c ^ (r % 32): 32 lanes that
@@ -133,12 +175,14 @@ __device__ __forceinline__ void gstage_flush(const char* lds, rsrc_t rslot, int 
 // B = h, so the tile is z^T: vocabulary on M, tokens on N), forms
 // G[token][v] and stores it as the member's two K-tiles of the round's slot
 // [256 tokens][K].  Then every member accumulates
-//   dh[rows][c0 .. c0+128] += slot[256][K] * W^T[c0 .. c0+128][round's vocabulary]
+//   dh[rows][c0 .. c0+HS] += slot[256][K] * W^T[c0 .. c0+HS][round's vocabulary]
 // with K = 128 * (K-tiles in the round).
+template <int HS>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
-  using P = BwdProducer;
-  using C = BwdConsumer;
-  __shared__ __attribute__((aligned(16))) char lds[kBwdLds];
+  using P = typename BwdCfg<HS>::P;
+  using C = typename BwdCfg<HS>::C;
+  constexpr bool kPark = BwdCfg<HS>::kPark;
+  __shared__ __attribute__((aligned(16))) char lds[BwdCfg<HS>::kLds];
   __shared__ int s_flag;
 
   const int s = p.group_size;
@@ -148,7 +192,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   const int wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t H = p.H, V = p.V, L = p.L;
-  const int64_t c0 = (int64_t)j * kSlice;
+  const int64_t c0 = (int64_t)j * HS;
+  float* const park = p.park + (int64_t)blockIdx.x * (kParkPerWG / 4);  // this workgroup's parking area (HS = 256)
   const int64_t slot_elems = (int64_t)s * 256 * 256;  // 2s K-tiles of [256][128]
   const int vt256 = (int)((V + 255) / 256);
   const int vt128 = (int)((V + 127) / 128);
@@ -176,7 +221,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
     const Operand oh = linear_operand(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
 
     f32x16 dacc[C::MB][C::NB];
-    zero_acc(dacc);
+    if constexpr (!kPark) zero_acc(dacc);
     for (int k = 0; k < rounds; ++k, ++epoch) {
       u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
       const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
@@ -214,18 +259,25 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
         __syncthreads();
         gstage_flush(lds, rslot, j);
       }
+      if constexpr (kPark) {
+        if (k == 0) zero_acc(dacc);
+        else unpark_acc(dacc, park, wave, lane);
+      }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
         return;
       const int ntl = min(2 * s, vt128 - k * 2 * s);
       const int64_t vbase = (int64_t)k * s * 256;
       // A: the slot's K-tiles [256][128]; B: W^T tiles [H][128] of the round's
-      // vocabulary, rows c0 .. c0+128 (K-tiled)
+      // vocabulary, rows c0 .. c0+HS (K-tiled)
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
              tiled_operand(p.WT + (vbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
              lds, dacc);
+      if constexpr (kPark) {
+        if (k + 1 < rounds) park_acc(dacc, park, wave, lane);
+      }
     }
     // dh[r][c] for r < L (waves: wm token quarter, wn column half)
-    store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * 64, lane);
+    store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
   }
 }
 
@@ -234,11 +286,13 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
 // of tokens [(k*s + j)*256, +256) against the group's vocabulary rows (A = h,
 // B = W: tokens on M, vocabulary on N), forms G^T[v][token] and stores it as
 // the member's two K-tiles of the round's slot [256 v][K].  Then
-//   dW[v rows][c0 .. c0+128] += slot[256][K] * h^T[c0 .. c0+128][round's tokens].
+//   dW[v rows][c0 .. c0+HS] += slot[256][K] * h^T[c0 .. c0+HS][round's tokens].
+template <int HS>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
-  using P = BwdProducer;
-  using C = BwdConsumer;
-  __shared__ __attribute__((aligned(16))) char lds[kBwdLds];
+  using P = typename BwdCfg<HS>::P;
+  using C = typename BwdCfg<HS>::C;
+  constexpr bool kPark = BwdCfg<HS>::kPark;
+  __shared__ __attribute__((aligned(16))) char lds[BwdCfg<HS>::kLds];
   __shared__ float row_lse2[256], row_scale[256];
   __shared__ int row_lab[256];  // label - v0 of the group's vocabulary block, or -1
   __shared__ int s_flag;
@@ -250,7 +304,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   const int wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t H = p.H, V = p.V, L = p.L;
-  const int64_t c0 = (int64_t)j * kSlice;
+  const int64_t c0 = (int64_t)j * HS;
+  float* const park = p.park + (int64_t)blockIdx.x * (kParkPerWG / 4);  // this workgroup's parking area (HS = 256)
   const int64_t slot_elems = (int64_t)s * 256 * 256;
   const int rt256 = (int)((L + 255) / 256);
   const int rt128 = (int)((L + 127) / 128);
@@ -264,7 +319,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
     const int64_t v0 = (int64_t)vb * 256;
     const Operand ow = linear_operand(p.W + v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
     f32x16 dacc[C::MB][C::NB];
-    zero_acc(dacc);
+    if constexpr (!kPark) zero_acc(dacc);
     for (int k = 0; k < rounds; ++k, ++epoch) {
       u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
       const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
@@ -322,6 +377,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
         __syncthreads();
         gstage_flush(lds, rslot, j);
       }
+      if constexpr (kPark) {
+        if (k == 0) zero_acc(dacc);
+        else unpark_acc(dacc, park, wave, lane);
+      }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
         return;
       const int ntl = min(2 * s, rt128 - k * 2 * s);
@@ -329,8 +388,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
              tiled_operand(p.hT + (rbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
              lds, dacc);
+      if constexpr (kPark) {
+        if (k + 1 < rounds) park_acc(dacc, park, wave, lane);
+      }
     }
-    store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, dacc, wm * 64, wn * 64, lane);
+    store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
   }
 }
 
@@ -347,11 +409,13 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
-const void* bwd_kernel(bool dh) {
-  return dh ? reinterpret_cast<const void*>(&k_bwd_dh) : reinterpret_cast<const void*>(&k_bwd_dW);
+const void* bwd_kernel(bool dh, int hs) {
+  if (hs == 256)
+    return dh ? reinterpret_cast<const void*>(&k_bwd_dh<256>) : reinterpret_cast<const void*>(&k_bwd_dW<256>);
+  return dh ? reinterpret_cast<const void*>(&k_bwd_dh<128>) : reinterpret_cast<const void*>(&k_bwd_dW<128>);
 }
 
-hipError_t bwd_resident_wgs(bool dh, int* wgs) {
+hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs) {
   int dev = 0, cus = 0, per = 0, coop = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -360,16 +424,16 @@ hipError_t bwd_resident_wgs(bool dh, int* wgs) {
   e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
   if (e != hipSuccess) return e;
   if (!coop) return hipErrorNotSupported;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_kernel(dh), kBwdThreads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_kernel(dh, hs), kBwdThreads, 0);
   if (e != hipSuccess) return e;
   *wgs = cus * per;
   return hipSuccess;
 }
 
-hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int n_wgs, hipStream_t st) {
+hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int hs, int n_wgs, hipStream_t st) {
   BwdArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchCooperativeKernel(bwd_kernel(dh), dim3((unsigned)n_wgs), dim3(kBwdThreads), args, 0, st);
+  return hipLaunchCooperativeKernel(bwd_kernel(dh, hs), dim3((unsigned)n_wgs), dim3(kBwdThreads), args, 0, st);
 }
 
 }  // namespace lmce

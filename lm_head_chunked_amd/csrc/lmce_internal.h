@@ -14,6 +14,7 @@ constexpr int kVTile = 256;         // vocabulary rows per forward logit tile
 constexpr int kSyncStride = 64;     // u32 words between two groups' counters (256 bytes)
 constexpr int kMaxBwdWGs = 256;     // upper bound of a backward cooperative grid
 constexpr int kXbufPerWG = 2 * 256 * 256 * 2;  // exchange bytes per backward workgroup (2 slots x one 256 x 256 bf16 tile)
+constexpr int kParkPerWG = 256 * 256 * 4;      // parked 256 x 256 fp32 accumulator slice per backward workgroup
 
 // First 256 bytes of the workspace.
 struct WsHeader {
@@ -50,11 +51,12 @@ struct BwdArgs {
   const uint16_t* hT;   // h transposed tile-major: [Lpad/128][H][128], zero past L
   const uint16_t* WT;   // W transposed tile-major: [Vpad/128][H][128], zero past V
   int64_t L, H, V, ignore_index, Lpad, Vpad;
-  int group_size;       // workgroups per group = H / 128
+  int group_size;       // workgroups per group = H / HS (HS = 256 if H % 256 == 0, else 128)
   int n_groups;
   int spin_limit;       // bound of every group wait
   unsigned* sync;       // [n_groups * kSyncStride] arrival counters, zeroed before the launch
   uint16_t* xbuf;       // [n_groups][2][2 * group_size][256][128] exchange slots
+  float* park;          // [workgroups][256 x 256] parked accumulators (HS = 256 only)
   WsHeader* hdr;
   float* dh;
   float* dW;
@@ -65,7 +67,7 @@ hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int6
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
 hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
-hipError_t bwd_resident_wgs(bool dh, int* wgs);
-hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int n_wgs, hipStream_t st);
+hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs);
+hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int hs, int n_wgs, hipStream_t st);
 
 }  // namespace lmce
