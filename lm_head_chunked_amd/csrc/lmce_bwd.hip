@@ -106,38 +106,35 @@ struct BwdCfg {
   static constexpr int kLds = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
 };
 
-// Parking area of one workgroup: for each wave, each 16-byte group q of a
-// lane's accumulator registers is one contiguous KiB (lane-major inside), so
-// every transfer instruction moves a whole KiB.  Plain global accesses: the
-// same lane reads back what it wrote.
+// Parking area of one workgroup: accumulator register r of lane l of wave w
+// at float index (w * R + r) * 64 + l (R registers per lane), moved with
+// 4-byte buffer accesses: the lane part is one vector offset, the register
+// part an immediate offset, the block of 16 registers the scalar offset, so
+// no address register stays live across the transfers and they pipeline.
 template <int MB, int NB>
-__device__ __forceinline__ void park_acc(const f32x16 (&acc)[MB][NB], float* area, int wave, int lane) {
-  float4* dst = reinterpret_cast<float4*>(area) + wave * MB * NB * 4 * 64 + lane;
+__device__ __forceinline__ void park_acc(const f32x16 (&acc)[MB][NB], rsrc_t rs, int wave, int lane) {
+  const uint32_t voff = (uint32_t)lane * 4u;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dst[((mb * NB + nb) * 4 + q) * 64] =
-            make_float4(acc[mb][nb][4 * q], acc[mb][nb][4 * q + 1], acc[mb][nb][4 * q + 2], acc[mb][nb][4 * q + 3]);
+      for (int e = 0; e < 16; ++e)
+        store_b32(rs, voff + (uint32_t)e * 256u, (uint32_t)((wave * MB * NB + mb * NB + nb) * 4096), acc[mb][nb][e]);
 }
 
 template <int MB, int NB>
-__device__ __forceinline__ void unpark_acc(f32x16 (&acc)[MB][NB], const float* area, int wave, int lane) {
-  const float4* src = reinterpret_cast<const float4*>(area) + wave * MB * NB * 4 * 64 + lane;
+__device__ __forceinline__ void unpark_acc(f32x16 (&acc)[MB][NB], rsrc_t rs, int wave, int lane) {
+  const uint32_t voff = (uint32_t)lane * 4u;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = src[((mb * NB + nb) * 4 + q) * 64];
-        acc[mb][nb][4 * q] = v.x;
-        acc[mb][nb][4 * q + 1] = v.y;
-        acc[mb][nb][4 * q + 2] = v.z;
-        acc[mb][nb][4 * q + 3] = v.w;
-      }
+      for (int e = 0; e < 16; ++e)
+        acc[mb][nb][e] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff + (uint32_t)e * 256u,
+                                                        (uint32_t)((wave * MB * NB + mb * NB + nb) * 4096), 0));
 }
 
 // A member's G tile is staged in LDS as [256 rows][256 K] bf16 (512 bytes
@@ -193,7 +190,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t H = p.H, V = p.V, L = p.L;
   const int64_t c0 = (int64_t)j * HS;
-  float* const park = p.park + (int64_t)blockIdx.x * (kParkPerWG / 4);  // this workgroup's parking area (HS = 256)
+  const rsrc_t park = make_rsrc(p.park + (int64_t)blockIdx.x * (kParkPerWG / 4), kPark ? kParkPerWG : 0);  // this workgroup's parking area
   const int64_t slot_elems = (int64_t)s * 256 * 256;  // 2s K-tiles of [256][128]
   const int vt256 = (int)((V + 255) / 256);
   const int vt128 = (int)((V + 127) / 128);
@@ -305,7 +302,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t H = p.H, V = p.V, L = p.L;
   const int64_t c0 = (int64_t)j * HS;
-  float* const park = p.park + (int64_t)blockIdx.x * (kParkPerWG / 4);  // this workgroup's parking area (HS = 256)
+  const rsrc_t park = make_rsrc(p.park + (int64_t)blockIdx.x * (kParkPerWG / 4), kPark ? kParkPerWG : 0);  // this workgroup's parking area
   const int64_t slot_elems = (int64_t)s * 256 * 256;
   const int rt256 = (int)((L + 255) / 256);
   const int rt128 = (int)((L + 127) / 128);
