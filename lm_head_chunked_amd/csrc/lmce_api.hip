@@ -21,7 +21,7 @@ struct Plan {
   int64_t L, H, V;
   int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
   int64_t Lpad, Vpad;
-  int hs, group_size, xbuf_wgs;
+  int hs, xbuf_wgs;
   size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, total;
 };
 
@@ -56,8 +56,10 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->xcd_map = (p->segments == 8 && p->ntiles % 32 == 0) ? 1 : 0;
   p->Lpad = (L + 127) / 128 * 128;
   p->Vpad = (V + 127) / 128 * 128;
-  p->hs = (H % 256 == 0) ? 256 : 128;  // H slice of one backward workgroup
-  p->group_size = (int)(H / p->hs);
+  // Widest H slice of one backward workgroup.  A 256-wide slice parks its
+  // accumulator (256 KiB out and back per round); the round's work grows with
+  // H, so the move pays off only for wide hidden sizes.
+  p->hs = (H % 256 == 0 && H >= 3072) ? 256 : 128;
 
   size_t off = align256(sizeof(WsHeader));
   p->off_pm = off;
@@ -76,7 +78,7 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   // Exchange slots for as many backward workgroups as can be useful (at most
   // one group per row block or vocabulary block, at most kMaxBwdWGs).
   const int64_t items = (L + 255) / 256 > (V + 255) / 256 ? (L + 255) / 256 : (V + 255) / 256;
-  int64_t wgs = items * p->group_size;
+  int64_t wgs = items * (H / 128);  // enough for either slice width
   if (wgs > kMaxBwdWGs) wgs = kMaxBwdWGs;
   p->xbuf_wgs = (int)wgs;
   off = align256(off + (size_t)wgs * kXbufPerWG);
@@ -195,7 +197,6 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
   a.ignore_index = ignore_index;
   a.Lpad = p.Lpad;
   a.Vpad = p.Vpad;
-  a.group_size = p.group_size;
   a.spin_limit = kSpinLimit;
   a.sync = at<unsigned>(workspace, p.off_sync);
   a.xbuf = at<uint16_t>(workspace, p.off_xbuf);
@@ -206,16 +207,27 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
   for (int pass = 0; pass < 2; ++pass) {
     const bool dh = pass == 0;
     if (!(which & (dh ? 1 : 2))) continue;
-    int resident = 0;
-    if (bwd_resident_wgs(dh, p.hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
-    if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
     const int64_t items = dh ? (L + 255) / 256 : (V + 255) / 256;  // row blocks or vocabulary blocks
-    int64_t groups = resident / p.group_size;
+    int hs = p.hs;
+    int resident = 0;
+    if (bwd_resident_wgs(dh, hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
+    if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
+    // 256-wide slices run both GEMMs on square tiles, but a group then holds
+    // half as many workgroups: with fewer blocks than groups, half the chip
+    // would idle, so such a pass takes 128-wide slices.
+    if (hs == 256 && items < resident / (H / 256)) {
+      hs = 128;
+      if (bwd_resident_wgs(dh, hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
+      if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
+    }
+    const int group_size = (int)(H / hs);
+    int64_t groups = resident / group_size;
     if (groups > items) groups = items;
     if (groups < 1) return LMCE_ERR_UNSUPPORTED;
+    a.group_size = group_size;
     a.n_groups = (int)groups;
     if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
-    if (launch_bwd_group(dh, a, p.hs, (int)groups * p.group_size, s) != hipSuccess) return LMCE_ERR_HIP;
+    if (launch_bwd_group(dh, a, hs, (int)groups * group_size, s) != hipSuccess) return LMCE_ERR_HIP;
   }
   return LMCE_OK;
 }

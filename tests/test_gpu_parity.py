@@ -100,6 +100,27 @@ def test_ragged_shapes(L, H, V, ign):
     assert_parity(gpu, ref, f"L={L} H={H} V={V}")
 
 
+# Wide hidden sizes (H % 256 == 0, H >= 3072) give each backward workgroup a
+# 256-wide slice whose accumulator is parked between rounds, when the pass has
+# at least one row block (dh) or vocabulary block (dW) per group: many rows
+# exercise the dh pass that way, a large vocabulary the dW pass.
+WIDE = [
+    (5500, 3072, 2500, 0.1),
+    (600, 3072, 5500, 0.1),
+]
+
+
+@pytest.mark.parametrize("L,H,V,ign", WIDE)
+def test_wide_slices(L, H, V, ign):
+    say(f"[case] wide slices L={L} H={H} V={V} ignore={ign}")
+    h, W, y = synth.random_case(L, H, V, seed=L + 7, w_std=0.02, ignore_frac=ign)
+    gpu = run_gpu(h, W, y, chunk_rows=256)
+    ref = oracle.fwd_bwd(np32(h), np32(W), y.numpy())
+    assert_parity(gpu, ref, f"L={L} H={H} V={V}")
+    ign_rows = (y == -100).numpy()
+    assert np.all(gpu["dh"][ign_rows] == 0.0)
+
+
 def test_results_do_not_depend_on_chunk_rows():
     say("[case] chunk_rows independence L=700 H=256 V=3000")
     h, W, y = synth.random_case(700, 256, 3000, seed=5, ignore_frac=0.1)
