@@ -70,9 +70,10 @@ const char* lmce_strerror(int status);
 /*
  * Bytes of device workspace that lmce_fwd / lmce_bwd need for this shape:
  * transposed bf16 copies of h and W for the backward ((L + V) * H * 2 bytes,
- * rounded up to 128 rows), per-row forward partials (O(L) floats), and a
- * fixed exchange ring for the backward (at most 64 MiB).  It never holds an
- * L x V array.  Writes the size to *bytes.  Returns LMCE_OK or a shape error.
+ * rounded up to 128 rows), per-row forward partials (O(L) floats), a fixed
+ * exchange ring for the backward (at most 64 MiB) and, for H >= 3072, a
+ * parking area for backward accumulators (at most 64 MiB).  It never holds
+ * an L x V array.  Writes the size to *bytes.  Returns LMCE_OK or a shape error.
  */
 int lmce_workspace_size(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, size_t* bytes);
 
@@ -105,9 +106,9 @@ int lmce_fwd(const void* h, const void* W, const int64_t* labels,
  * h and W, turned into bf16 G and contracted in the same round into
  *   dh_out fp32 [L, H] = G W     (overwritten, not accumulated)
  *   dW_out fp32 [V, H] = G^T h   (overwritten, not accumulated)
- * by the co-resident workgroups that own the 128-wide H slices of the
- * outputs; a G tile lives only in the workspace's exchange ring for the one
- * round that consumes it.  The device must support cooperative launches
+ * by the co-resident workgroups that own the 128- or 256-wide H slices of
+ * the outputs; a G tile lives only in the workspace's exchange ring for the
+ * one round that consumes it.  The device must support cooperative launches
  * (otherwise LMCE_ERR_HIP or LMCE_ERR_UNSUPPORTED).
  *
  *   lse        fp32 [L]  the lse_out of lmce_fwd on the same inputs
