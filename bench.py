@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the fused LM-head + cross-entropy loss, forward + backward, on one MI355X.
 
-One step = lmce_fwd (loss, per-row lse) + lmce_bwd_dh + lmce_bwd_dW (together
-exactly lmce_bwd) over the whole workload, inputs already resident in HBM.
-Default workload: the Qwen3-8B head at one GPU's share of a 1,048,576-token
-sequence (L = 131072, H = 4096, V = 151936, Zipf(1.1) labels, row 0 ignored),
-synthetic and seeded.
+One step = one training forward and backward over the whole workload, inputs
+already resident in HBM.  By default that is the training pair
+lmce_fwd_train + lmce_bwd_train (the forward's vocabulary sweep also yields
+the dh contraction); --pair plain times lmce_fwd + lmce_bwd_dh + lmce_bwd_dW
+instead.  Default workload: the Qwen3-8B head at one GPU's share of a
+1,048,576-token sequence (L = 131072, H = 4096, V = 151936, Zipf(1.1)
+labels, row 0 ignored), synthetic and seeded.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value            tokens/s of the whole step (L * steps / wall time)
@@ -15,11 +17,13 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                    launched on): algorithmic flops per launch / its mean duration
   cpu_baseline     the fp64 CPU oracle timed on a bounded sample of the workload
 
-Flop accounting (algorithmic, independent of the schedule):
-  forward      2 L H V            (logits of every row; lse is returned for all)
-  backward     6 N H V            (logit recompute, dh = G W, dW = G^T h; N valid rows)
-  lmce_bwd_dh  3 N H V            (half of the recompute + the dh contraction)
-  lmce_bwd_dW  3 N H V            (half of the recompute + the dW contraction)
+Flop accounting (algorithmic, independent of the schedule; N valid rows):
+  whole step       2 L H V + 6 N H V   (logits of every row; recompute, dh = G W, dW = G^T h)
+  lmce_fwd_train   2 L H V + 2 N H V   (logits, and the dh contraction sum_v softmax W_v)
+  lmce_bwd_train   4 N H V             (logit recompute and the dW contraction)
+  lmce_fwd         2 L H V
+  lmce_bwd_dh      3 N H V             (half of the recompute + the dh contraction)
+  lmce_bwd_dW      3 N H V             (half of the recompute + the dW contraction)
 """
 
 import argparse
@@ -100,6 +104,8 @@ def main():
     ap.add_argument("--chunk-rows", type=int, default=None)
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pair", choices=["train", "plain"], default="train",
+                    help="train: lmce_fwd_train + lmce_bwd_train; plain: lmce_fwd + lmce_bwd_dh + lmce_bwd_dW")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (scale for HBM byte counters) and exit")
     args = ap.parse_args()
@@ -148,24 +154,42 @@ def main():
     base_alloc = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
 
+    plain = args.pair == "plain"
+    # (name, kernel that dominates the call, algorithmic flops) per call of a step
+    f_fwd = 2.0 * L * H * V
+    f_nhv = 1.0 * n_valid * H * V
+    if plain:
+        calls = [("lmce_fwd", "k_fwd", f_fwd), ("lmce_bwd_dh", "k_bwd_dh", 3 * f_nhv),
+                 ("lmce_bwd_dW", "k_bwd_dW", 3 * f_nhv)]
+    else:
+        calls = [("lmce_fwd_train", "k_fwd_dh", f_fwd + 2 * f_nhv), ("lmce_bwd_train", "k_bwd_dW", 4 * f_nhv)]
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        lm.lmce_fwd(h, W, y, -100, chunk, ws, loss, lse)
-        if ev is not None:
-            ev[1].record(stream)
-        lm.lmce_bwd_dh(h, W, y, lse, g, -100, chunk, ws, dh)
-        if ev is not None:
-            ev[2].record(stream)
-        lm.lmce_bwd_dW(h, W, y, lse, g, -100, chunk, ws, dW)
-        if ev is not None:
-            ev[3].record(stream)
+        if plain:
+            lm.lmce_fwd(h, W, y, -100, chunk, ws, loss, lse)
+            if ev is not None:
+                ev[1].record(stream)
+            lm.lmce_bwd_dh(h, W, y, lse, g, -100, chunk, ws, dh)
+            if ev is not None:
+                ev[2].record(stream)
+            lm.lmce_bwd_dW(h, W, y, lse, g, -100, chunk, ws, dW)
+            if ev is not None:
+                ev[3].record(stream)
+        else:
+            lm.lmce_fwd_train(h, W, y, -100, chunk, ws, loss, lse)
+            if ev is not None:
+                ev[1].record(stream)
+            lm.lmce_bwd_train(h, W, y, lse, g, -100, chunk, ws, dh, dW)
+            if ev is not None:
+                ev[2].record(stream)
 
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
         log(f"[bench] warmup {i + 1}/{args.warmup} done")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -176,25 +200,16 @@ def main():
     if status != _lib.LMCE_OK:
         raise RuntimeError(f"lmce status {status}: {_lib.strerror(status)}")
     peak_extra = torch.cuda.max_memory_allocated(dev) - base_alloc
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    dh_ms = [e[1].elapsed_time(e[2]) for e in events]
-    dW_ms = [e[2].elapsed_time(e[3]) for e in events]
+    call_ms = [statistics.mean(e[c].elapsed_time(e[c + 1]) for e in events) for c in range(len(calls))]
     ms_step = wall * 1000.0 / args.steps
-    log(f"[bench] {args.steps} steps: {ms_step:.1f} ms/step; fwd {statistics.mean(fwd_ms):.1f} ms, "
-        f"bwd_dh {statistics.mean(dh_ms):.1f} ms, bwd_dW {statistics.mean(dW_ms):.1f} ms; loss {float(loss):.5f}")
+    log(f"[bench] {args.steps} steps: {ms_step:.1f} ms/step; " +
+        ", ".join(f"{c[0]} {t:.1f} ms" for c, t in zip(calls, call_ms)) + f"; loss {float(loss):.5f}")
 
-    f_fwd = 2.0 * L * H * V
-    f_half_bwd = 3.0 * n_valid * H * V
-    f_alg = f_fwd + 2 * f_half_bwd
+    f_alg = f_fwd + 6 * f_nhv
     tflops = f_alg / (ms_step / 1000.0) / 1e12
-    calls = {
-        "lmce_fwd": (f_fwd, statistics.mean(fwd_ms)),
-        "lmce_bwd_dh": (f_half_bwd, statistics.mean(dh_ms)),
-        "lmce_bwd_dW": (f_half_bwd, statistics.mean(dW_ms)),
-    }
-    dom = max(calls, key=lambda k: calls[k][1])
-    dom_kernel = {"lmce_fwd": "k_fwd", "lmce_bwd_dh": "k_bwd_dh", "lmce_bwd_dW": "k_bwd_dW"}[dom]
-    dom_tflops = calls[dom][0] / (calls[dom][1] / 1000.0) / 1e12
+    dom = max(range(len(calls)), key=lambda c: call_ms[c])
+    dom_name, dom_kernel, dom_flops = calls[dom]
+    dom_tflops = dom_flops / (call_ms[dom] / 1000.0) / 1e12
 
     result = {
         "metric": METRIC,
@@ -212,15 +227,15 @@ def main():
         "config": {
             "workload": wl.name, "L": L, "H": H, "V": V, "n_valid": n_valid, "chunk_rows": chunk,
             "labels": wl.labels, "achieved_tflops": tflops, "peak_frac_bf16": tflops / PEAK_BF16_TFLOPS,
-            "fwd_ms": statistics.mean(fwd_ms), "bwd_dh_ms": statistics.mean(dh_ms),
-            "bwd_dW_ms": statistics.mean(dW_ms), "workspace_bytes": ws_bytes,
-            "peak_extra_alloc_bytes": int(peak_extra), "logits_fp32_bytes_avoided": L * V * 4,
+            "pair": args.pair, "call_ms": {c[0]: t for c, t in zip(calls, call_ms)},
+            "workspace_bytes": ws_bytes, "peak_extra_alloc_bytes": int(peak_extra),
+            "logits_fp32_bytes_avoided": L * V * 4,
             "loss": float(loss), "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "mfma", "kernel": dom_kernel, "call": dom, "achieved": dom_tflops,
+            "bound": "mfma", "kernel": dom_kernel, "call": dom_name, "achieved": dom_tflops,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
-            "traffic": recorded_traffic(wl.name, dom_kernel), "mean_ms": calls[dom][1],
+            "traffic": recorded_traffic(wl.name, dom_kernel), "mean_ms": call_ms[dom],
         },
         "cpu_baseline": None,
     }

@@ -58,7 +58,8 @@ typedef enum {
   LMCE_ERR_UNSUPPORTED = -3, /* H % 128 != 0, chunk_rows not a multiple of 32 in [32, 1024], or the device cannot run the grid */
   LMCE_ERR_WORKSPACE = -4,   /* workspace_bytes smaller than lmce_workspace_size() */
   LMCE_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
-  LMCE_ERR_LABEL = -6        /* (asynchronous) a label is outside [0, V) and not ignore_index */
+  LMCE_ERR_LABEL = -6,       /* (asynchronous) a label is outside [0, V) and not ignore_index */
+  LMCE_ERR_STATE = -7        /* (asynchronous) lmce_bwd_train without a preceding lmce_fwd_train on the workspace */
 } lmce_status;
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -72,8 +73,8 @@ const char* lmce_strerror(int status);
  * transposed bf16 copies of h and W for the backward ((L + V) * H * 2 bytes,
  * rounded up to 128 rows), per-row forward partials (O(L) floats), a fixed
  * exchange ring for the backward (at most 64 MiB) and, for H >= 3072, a
- * parking area for backward accumulators (at most 64 MiB).  It never holds
- * an L x V array.  Writes the size to *bytes.  Returns LMCE_OK or a shape error.
+ * parking area for backward accumulators (at most 64 MiB), and the training
+ * forward's O (L * H * 4 bytes).  It never holds an L x V array.  Writes the size to *bytes.  Returns LMCE_OK or a shape error.
  */
 int lmce_workspace_size(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, size_t* bytes);
 
@@ -136,11 +137,34 @@ int lmce_bwd_dW(const void* h, const void* W, const int64_t* labels, const float
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Training pair.  Same page and sections, same results as lmce_fwd followed
+ * by lmce_bwd, with less work: the forward's single vocabulary sweep also
+ * accumulates O_i = sum_v softmax(z_i)_v W_v with a running-maximum rescale
+ * (the gradient of the mean NLL is dh_i = g/N * valid_i * (O_i - W_{y_i})),
+ * and keeps O (fp32 [L, H]) in the workspace.  lmce_bwd_train then forms dh
+ * from O without recomputing any logit and runs the dW pass.
+ *
+ * lmce_fwd_train: arguments and outputs as lmce_fwd.
+ * lmce_bwd_train: arguments and outputs as lmce_bwd.  It must follow an
+ *   lmce_fwd_train on the same inputs, workspace and stream, with no other
+ *   lmce_fwd in between; otherwise dh_out is NaN and lmce_read_status()
+ *   returns LMCE_ERR_STATE.
+ */
+int lmce_fwd_train(const void* h, const void* W, const int64_t* labels,
+                   int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
+                   float* loss_out, float* lse_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+int lmce_bwd_train(const void* h, const void* W, const int64_t* labels, const float* lse,
+                   int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
+                   const float* grad_loss, float* dh_out, float* dW_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Synchronises `stream` and returns the asynchronous status recorded in the
- * workspace by the last lmce_fwd / lmce_bwd on it: LMCE_OK, LMCE_ERR_LABEL,
- * or LMCE_ERR_HIP if the synchronisation failed or a backward workgroup
- * gave up waiting for the other members of its group (a bounded wait; the
- * gradients are then incomplete).
+ * workspace by the last calls on it: LMCE_OK, LMCE_ERR_LABEL, LMCE_ERR_STATE,
+ * or LMCE_ERR_HIP if the synchronisation failed or a group-scheduled
+ * workgroup gave up waiting for the other members of its group (a bounded
+ * wait; the results are then incomplete).
  */
 int lmce_read_status(const void* workspace, void* stream);
 

@@ -26,6 +26,8 @@ __all__ = [
     "lmce_bwd",
     "lmce_bwd_dh",
     "lmce_bwd_dW",
+    "lmce_fwd_train",
+    "lmce_bwd_train",
     "lmce_read_status",
     "chunked_nll",
     "LmceError",
@@ -82,6 +84,45 @@ def lmce_fwd(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_R
     return loss, lse
 
 
+def lmce_fwd_train(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS, workspace=None,
+                   loss_out=None, lse_out=None):
+    """As lmce_fwd, and also leaves in `workspace` what lmce_bwd_train needs
+    to form dh without recomputing the logits.  Pass the same workspace on."""
+    L, H, V = _check_inputs(h, W, labels)
+    dev = h.device
+    if workspace is None:
+        raise ValueError("lmce_fwd_train needs an explicit workspace to hand to lmce_bwd_train")
+    ws = _workspace(L, H, V, chunk_rows, dev, workspace)
+    loss = torch.empty((), dtype=torch.float32, device=dev) if loss_out is None else loss_out
+    lse = torch.empty(L, dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    st = _lib.fwd_train(h.data_ptr(), W.data_ptr(), labels.data_ptr(), L, H, V, ignore_index, chunk_rows,
+                        loss.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(st, "lmce_fwd_train")
+    return loss, lse
+
+
+def lmce_bwd_train(h, W, labels, lse, grad_loss=None, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS,
+                   workspace=None, dh_out=None, dW_out=None):
+    """dh and dW like lmce_bwd, after lmce_fwd_train on the same inputs and workspace."""
+    L, H, V = _check_inputs(h, W, labels)
+    dev = h.device
+    if lse.dtype != torch.float32 or lse.shape != (L,) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [L]")
+    if workspace is None:
+        raise ValueError("lmce_bwd_train needs the workspace of lmce_fwd_train")
+    if grad_loss is None:
+        grad_loss = torch.ones((), dtype=torch.float32, device=dev)
+    grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
+    ws = _workspace(L, H, V, chunk_rows, dev, workspace)
+    dh = torch.empty(L, H, dtype=torch.float32, device=dev) if dh_out is None else dh_out
+    dW = torch.empty(V, H, dtype=torch.float32, device=dev) if dW_out is None else dW_out
+    st = _lib.bwd_train(h.data_ptr(), W.data_ptr(), labels.data_ptr(), lse.data_ptr(), L, H, V, ignore_index,
+                        chunk_rows, grad_loss.data_ptr(), dh.data_ptr(), dW.data_ptr(), ws.data_ptr(),
+                        ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(st, "lmce_bwd_train")
+    return dh, dW
+
+
 def lmce_bwd(h, W, labels, lse, grad_loss=None, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS,
              workspace=None, dh_out=None, dW_out=None):
     """dh (fp32 [L, H]) and dW (fp32 [V, H]) of grad_loss * loss (overwritten)."""
@@ -134,7 +175,7 @@ def lmce_bwd_dW(h, W, labels, lse, grad_loss=None, ignore_index=IGNORE_INDEX, ch
 
 
 def lmce_read_status(workspace) -> int:
-    """Synchronises the current stream; LMCE_OK or LMCE_ERR_LABEL recorded by the last call."""
+    """Synchronises the current stream; the asynchronous status recorded by the last calls."""
     return _lib.read_status(workspace.data_ptr(), _stream(workspace.device))
 
 
@@ -143,7 +184,7 @@ class _ChunkedNLL(torch.autograd.Function):
     def forward(ctx, h, W, labels, ignore_index, chunk_rows):
         L, H, V = _check_inputs(h, W, labels)
         ws = _workspace(L, H, V, chunk_rows, h.device, None)
-        loss, lse = lmce_fwd(h, W, labels, ignore_index, chunk_rows, ws)
+        loss, lse = lmce_fwd_train(h, W, labels, ignore_index, chunk_rows, ws)
         ctx.save_for_backward(h, W, labels, lse)
         ctx.ignore_index = ignore_index
         ctx.chunk_rows = chunk_rows
@@ -153,7 +194,7 @@ class _ChunkedNLL(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_loss):
         h, W, labels, lse = ctx.saved_tensors
-        dh, dW = lmce_bwd(h, W, labels, lse, grad_loss, ctx.ignore_index, ctx.chunk_rows, ctx.ws)
+        dh, dW = lmce_bwd_train(h, W, labels, lse, grad_loss, ctx.ignore_index, ctx.chunk_rows, ctx.ws)
         ctx.ws = None
         return dh, dW, None, None, None
 

@@ -20,6 +20,7 @@ LMCE_ERR_UNSUPPORTED = -3
 LMCE_ERR_WORKSPACE = -4
 LMCE_ERR_HIP = -5
 LMCE_ERR_LABEL = -6
+LMCE_ERR_STATE = -7
 
 # Every symbol the public header declares, with (restype, argtypes).
 _c_i64 = ctypes.c_int64
@@ -36,6 +37,10 @@ SIGNATURES = {
                                    _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_bwd_dW": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                    _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "lmce_fwd_train": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                      _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "lmce_bwd_train": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                      _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_read_status": (ctypes.c_int, [_c_vp, _c_vp]),
 }
 
@@ -101,6 +106,18 @@ def bwd_dW(h_ptr, W_ptr, labels_ptr, lse_ptr, L, H, V, ignore_index, chunk_rows,
            stream):
     return load().lmce_bwd_dW(h_ptr, W_ptr, labels_ptr, lse_ptr, int(L), int(H), int(V), int(ignore_index),
                               int(chunk_rows), grad_ptr, dW_ptr, ws_ptr, int(ws_bytes), stream)
+
+
+def fwd_train(h_ptr, W_ptr, labels_ptr, L, H, V, ignore_index, chunk_rows, loss_ptr, lse_ptr, ws_ptr, ws_bytes,
+              stream):
+    return load().lmce_fwd_train(h_ptr, W_ptr, labels_ptr, int(L), int(H), int(V), int(ignore_index),
+                                 int(chunk_rows), loss_ptr, lse_ptr, ws_ptr, int(ws_bytes), stream)
+
+
+def bwd_train(h_ptr, W_ptr, labels_ptr, lse_ptr, L, H, V, ignore_index, chunk_rows, grad_ptr, dh_ptr, dW_ptr, ws_ptr,
+              ws_bytes, stream):
+    return load().lmce_bwd_train(h_ptr, W_ptr, labels_ptr, lse_ptr, int(L), int(H), int(V), int(ignore_index),
+                                 int(chunk_rows), grad_ptr, dh_ptr, dW_ptr, ws_ptr, int(ws_bytes), stream)
 
 
 def read_status(ws_ptr, stream) -> int:

@@ -22,7 +22,7 @@ struct Plan {
   int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
   int64_t Lpad, Vpad;
   int hs, xbuf_wgs;
-  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, total;
+  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, off_xstat, off_O, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -84,6 +84,11 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   off = align256(off + (size_t)wgs * kXbufPerWG);
   p->off_park = off;
   if (p->hs == 256) off = align256(off + (size_t)wgs * kParkPerWG);
+  p->off_xstat = off;
+  off = align256(off + (size_t)wgs * kXstatPerWG);
+  // training forward: O = sum_v softmax(z)_v W_v of every row, fp32 [L][H]
+  p->off_O = off;
+  off = align256(off + sizeof(float) * (size_t)L * (size_t)H);
   p->total = off;
   return LMCE_OK;
 }
@@ -111,6 +116,7 @@ extern "C" const char* lmce_strerror(int status) {
     case LMCE_ERR_WORKSPACE: return "workspace smaller than lmce_workspace_size()";
     case LMCE_ERR_HIP: return "HIP runtime error";
     case LMCE_ERR_LABEL: return "a label is outside [0, V) and is not ignore_index";
+    case LMCE_ERR_STATE: return "lmce_bwd_train without a preceding lmce_fwd_train on this workspace";
     default: return "unknown status";
   }
 }
@@ -137,7 +143,7 @@ extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   WsHeader* hdr = at<WsHeader>(workspace, 0);
-  if (launch_count_labels(labels, L, V, ignore_index, hdr, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (launch_count_labels(labels, L, V, ignore_index, hdr, 0, s) != hipSuccess) return LMCE_ERR_HIP;
   FwdArgs a;
   a.h = static_cast<const uint16_t*>(h);
   a.W = static_cast<const uint16_t*>(W);
@@ -164,6 +170,63 @@ extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int
 
 namespace {
 
+// One group-scheduled pass over `items` blocks (row blocks or vocabulary
+// blocks): picks the H slice width, sizes the cooperative grid to the
+// resident workgroups, resets the group counters and launches.
+int launch_group_pass(int pass, BwdArgs& a, const Plan& p, int64_t items, hipStream_t s) {
+  // The fused training forward always takes 128-wide slices: its 256-wide
+  // form (accumulator parked between rounds) gave results that differed
+  // from run to run, and stays disabled until that is understood.
+  int hs = pass == kPassFwdDh ? 128 : p.hs;
+  int resident = 0;
+  if (bwd_resident_wgs(pass, hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
+  if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
+  // 256-wide slices run both GEMMs on square tiles, but a group then holds
+  // half as many workgroups: with fewer blocks than groups, half the chip
+  // would idle, so such a pass takes 128-wide slices.
+  if (hs == 256 && items < resident / (p.H / 256)) {
+    hs = 128;
+    if (bwd_resident_wgs(pass, hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
+    if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
+  }
+  const int group_size = (int)(p.H / hs);
+  int64_t groups = resident / group_size;
+  if (groups > items) groups = items;
+  if (groups < 1) return LMCE_ERR_UNSUPPORTED;
+  a.group_size = group_size;
+  a.n_groups = (int)groups;
+  if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (launch_bwd_group(pass, a, hs, (int)groups * group_size, s) != hipSuccess) return LMCE_ERR_HIP;
+  return LMCE_OK;
+}
+
+// Arguments shared by the group-scheduled kernels (pointers into the workspace).
+BwdArgs group_args(const Plan& p, const void* h, const void* W, const int64_t* labels, int64_t ignore_index,
+                   void* workspace) {
+  BwdArgs a = {};
+  a.h = static_cast<const uint16_t*>(h);
+  a.W = static_cast<const uint16_t*>(W);
+  a.labels = labels;
+  a.hT = at<uint16_t>(workspace, p.off_hT);
+  a.WT = at<uint16_t>(workspace, p.off_WT);
+  a.L = p.L;
+  a.H = p.H;
+  a.V = p.V;
+  a.ignore_index = ignore_index;
+  a.Lpad = p.Lpad;
+  a.Vpad = p.Vpad;
+  a.spin_limit = kSpinLimit;
+  a.sync = at<unsigned>(workspace, p.off_sync);
+  a.xbuf = at<uint16_t>(workspace, p.off_xbuf);
+  a.park = at<float>(workspace, p.off_park);
+  a.xstat = at<float>(workspace, p.off_xstat);
+  a.O = at<float>(workspace, p.off_O);
+  a.part_m = at<float>(workspace, p.off_pm);
+  a.part_s = at<float>(workspace, p.off_ps);
+  a.hdr = at<WsHeader>(workspace, 0);
+  return a;
+}
+
 // Shared by lmce_bwd, lmce_bwd_dh and lmce_bwd_dW: which = 1 (dh), 2 (dW), 3 (both).
 int bwd_common(int which, const void* h, const void* W, const int64_t* labels, const float* lse, int64_t L,
                int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows, const float* grad_loss, float* dh_out,
@@ -178,56 +241,21 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   WsHeader* hdr = at<WsHeader>(workspace, 0);
-  if (launch_count_labels(labels, L, V, ignore_index, hdr, s) != hipSuccess) return LMCE_ERR_HIP;
-  uint16_t* hT = at<uint16_t>(workspace, p.off_hT);
-  uint16_t* WT = at<uint16_t>(workspace, p.off_WT);
-  if ((which & 2) && launch_transpose(h, L, H, hT, p.Lpad, s) != hipSuccess) return LMCE_ERR_HIP;
-  if ((which & 1) && launch_transpose(W, V, H, WT, p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
-  BwdArgs a;
-  a.h = static_cast<const uint16_t*>(h);
-  a.W = static_cast<const uint16_t*>(W);
-  a.labels = labels;
+  if (launch_count_labels(labels, L, V, ignore_index, hdr, -1, s) != hipSuccess) return LMCE_ERR_HIP;
+  BwdArgs a = group_args(p, h, W, labels, ignore_index, workspace);
   a.lse = lse;
   a.grad_loss = grad_loss;
-  a.hT = hT;
-  a.WT = WT;
-  a.L = L;
-  a.H = H;
-  a.V = V;
-  a.ignore_index = ignore_index;
-  a.Lpad = p.Lpad;
-  a.Vpad = p.Vpad;
-  a.spin_limit = kSpinLimit;
-  a.sync = at<unsigned>(workspace, p.off_sync);
-  a.xbuf = at<uint16_t>(workspace, p.off_xbuf);
-  a.park = at<float>(workspace, p.off_park);
-  a.hdr = hdr;
   a.dh = dh_out;
   a.dW = dW_out;
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool dh = pass == 0;
-    if (!(which & (dh ? 1 : 2))) continue;
-    const int64_t items = dh ? (L + 255) / 256 : (V + 255) / 256;  // row blocks or vocabulary blocks
-    int hs = p.hs;
-    int resident = 0;
-    if (bwd_resident_wgs(dh, hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
-    if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
-    // 256-wide slices run both GEMMs on square tiles, but a group then holds
-    // half as many workgroups: with fewer blocks than groups, half the chip
-    // would idle, so such a pass takes 128-wide slices.
-    if (hs == 256 && items < resident / (H / 256)) {
-      hs = 128;
-      if (bwd_resident_wgs(dh, hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
-      if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
-    }
-    const int group_size = (int)(H / hs);
-    int64_t groups = resident / group_size;
-    if (groups > items) groups = items;
-    if (groups < 1) return LMCE_ERR_UNSUPPORTED;
-    a.group_size = group_size;
-    a.n_groups = (int)groups;
-    if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
-    if (launch_bwd_group(dh, a, hs, (int)groups * group_size, s) != hipSuccess) return LMCE_ERR_HIP;
+  if ((which & 2) && launch_transpose(h, L, H, at<uint16_t>(workspace, p.off_hT), p.Lpad, s) != hipSuccess) return LMCE_ERR_HIP;
+  if ((which & 1) && launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (which & 1) {
+    st = launch_group_pass(kPassDh, a, p, (L + 255) / 256, s);
+    if (st != LMCE_OK) return st;
+  }
+  if (which & 2) {
+    st = launch_group_pass(kPassDw, a, p, (V + 255) / 256, s);
+    if (st != LMCE_OK) return st;
   }
   return LMCE_OK;
 }
@@ -255,6 +283,65 @@ extern "C" int lmce_bwd_dW(const void* h, const void* W, const int64_t* labels, 
                     workspace_bytes, stream);
 }
 
+extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* labels, int64_t L, int64_t H, int64_t V,
+                              int64_t ignore_index, int64_t chunk_rows, float* loss_out, float* lse_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(L, H, V, chunk_rows, &p);
+  if (st != LMCE_OK) return st;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(labels, 8) || !aligned(loss_out, 4) || !aligned(lse_out, 4) ||
+      !aligned(workspace, 256))
+    return LMCE_ERR_NULL;
+  if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  WsHeader* hdr = at<WsHeader>(workspace, 0);
+  if (launch_count_labels(labels, L, V, ignore_index, hdr, kSavedTag, s) != hipSuccess) return LMCE_ERR_HIP;
+  BwdArgs a = group_args(p, h, W, labels, ignore_index, workspace);
+  if (launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
+  st = launch_group_pass(kPassFwdDh, a, p, (L + 255) / 256, s);
+  if (st != LMCE_OK) return st;
+  // (max, sum) of every row came out as one log-sum-exp segment
+  FwdArgs f = {};
+  f.h = a.h;
+  f.W = a.W;
+  f.labels = labels;
+  f.L = L;
+  f.H = H;
+  f.V = V;
+  f.ignore_index = ignore_index;
+  f.chunk_rows = p.chunk_rows;
+  f.segments = 1;
+  f.hdr = hdr;
+  f.part_m = a.part_m;
+  f.part_s = a.part_s;
+  f.block_sum = at<float>(workspace, p.off_bsum);
+  if (launch_fwd_rows(f, loss_out, lse_out, s) != hipSuccess) return LMCE_ERR_HIP;
+  return LMCE_OK;
+}
+
+extern "C" int lmce_bwd_train(const void* h, const void* W, const int64_t* labels, const float* lse, int64_t L,
+                              int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows, const float* grad_loss,
+                              float* dh_out, float* dW_out, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(L, H, V, chunk_rows, &p);
+  if (st != LMCE_OK) return st;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(labels, 8) || !aligned(lse, 4) || !aligned(grad_loss, 4) ||
+      !aligned(dh_out, 16) || !aligned(dW_out, 16) || !aligned(workspace, 256))
+    return LMCE_ERR_NULL;
+  if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  BwdArgs a = group_args(p, h, W, labels, ignore_index, workspace);
+  a.lse = lse;
+  a.grad_loss = grad_loss;
+  a.dh = dh_out;
+  a.dW = dW_out;
+  if (launch_dh_finish(a, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (launch_transpose(h, L, H, at<uint16_t>(workspace, p.off_hT), p.Lpad, s) != hipSuccess) return LMCE_ERR_HIP;
+  return launch_group_pass(kPassDw, a, p, (V + 255) / 256, s);
+}
+
 extern "C" int lmce_read_status(const void* workspace, void* stream) {
   if (!aligned(workspace, 256)) return LMCE_ERR_NULL;
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return LMCE_ERR_HIP;
@@ -262,5 +349,6 @@ extern "C" int lmce_read_status(const void* workspace, void* stream) {
   if (hipMemcpy(&hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost) != hipSuccess) return LMCE_ERR_HIP;
   if (hdr.status & kStatusLabel) return LMCE_ERR_LABEL;
   if (hdr.status & kStatusSync) return LMCE_ERR_HIP;
+  if (hdr.status & kStatusState) return LMCE_ERR_STATE;
   return LMCE_OK;
 }

@@ -269,12 +269,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
              tiled_operand(p.WT + (vbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
              lds, dacc);
-      if constexpr (kPark) {
-        if (k + 1 < rounds) park_acc(dacc, park, wave, lane);
-      }
+      if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
     }
     // dh[r][c] for r < L (waves: wm token quarter, wn column half)
-    store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
+    if constexpr (kPark) {
+      f32x16 fin[C::MB][C::NB];
+      unpark_acc(fin, park, wave, lane);
+      store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
+    } else {
+      store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
+    }
   }
 }
 
@@ -385,11 +389,256 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
              tiled_operand(p.hT + (rbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
              lds, dacc);
+      if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
+    }
+    if constexpr (kPark) {
+      f32x16 fin[C::MB][C::NB];
+      unpark_acc(fin, park, wave, lane);
+      store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
+    } else {
+      store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
+    }
+  }
+}
+
+// ----------------------------------------------------- fused training forward
+// Copies the staged tile like gstage_flush, scaling row r by fac[r] on the way.
+__device__ __forceinline__ void gstage_flush_scaled(const char* lds, const float* fac, rsrc_t rslot, int j) {
+  const int t = threadIdx.x;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int idx = i * 512 + t;
+    const int row = idx >> 5, c = idx & 31;
+    const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+        (const __attribute__((address_space(3))) char*)lds + row * 512 + ((c ^ (row & 31)) << 4));
+    const bf16x8 x = __builtin_bit_cast(bf16x8, v);
+    const float f = fac[row];
+    const f32x4 lo = {(float)x[0] * f, (float)x[1] * f, (float)x[2] * f, (float)x[3] * f};
+    const f32x4 hi = {(float)x[4] * f, (float)x[5] * f, (float)x[6] * f, (float)x[7] * f};
+    const bf16x4 blo = __builtin_convertvector(lo, bf16x4), bhi = __builtin_convertvector(hi, bf16x4);
+    const u32x4 w = {__builtin_bit_cast(u32x2, blo)[0], __builtin_bit_cast(u32x2, blo)[1],
+                     __builtin_bit_cast(u32x2, bhi)[0], __builtin_bit_cast(u32x2, bhi)[1]};
+    const uint32_t voff = (uint32_t)(((c >> 4) * 256 * 128 + row * 128 + (c & 15) * 8) * 2);
+    store_sc1_b128(rslot, voff, (uint32_t)j * 2u * 256u * 128u * 2u, w);
+  }
+}
+
+// One vocabulary sweep per 256-row block yields both the log-sum-exp of every
+// row and O = sum_v softmax(z)_v W_v, so that dh = g/N * (O - W_y) needs no
+// second sweep (the gradient of the mean NLL, the definition on the pages
+// above).  The structure is that of k_bwd_dh, with the softmax reference
+// taken on the fly as in an online softmax.  In round k each member computes
+// its logit tile, the tile's per-token maximum m_j, P_j = exp(z - m_j)
+// (staged in LDS as bf16) and the lane's sums of P_j; after a group barrier
+// all members read the s maxima and agree on the running maximum M_k of each
+// token; each member writes its P_j scaled by exp(m_j - M_k) to the exchange
+// and rescales its row sums; the contraction rescales its O slice by
+// exp(M_{k-1} - M_k) and adds the round's P W.  After the last round the row
+// sums are exchanged once more, O is divided by them and stored, and
+// (max, sum) go out as a one-segment log-sum-exp partial of every row.
+template <int HS>
+__global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
+  using P = typename BwdCfg<HS>::P;
+  using C = typename BwdCfg<HS>::C;
+  constexpr bool kPark = BwdCfg<HS>::kPark;
+  __shared__ __attribute__((aligned(16))) char lds[BwdCfg<HS>::kLds];
+  __shared__ float red[4][256];  // per-wave partial (max or sum) of each token
+  __shared__ float row_m[256];   // running maximum M of each token
+  __shared__ float row_l[256];   // this member's tile maximum m_j of each token
+  __shared__ float row_a[256];   // exp(M_old - M_new) (last: 1 / sum)
+  __shared__ float row_f[256];   // exp(m_j - M_new)
+  __shared__ int s_flag;
+
+  const int s = p.group_size;
+  const int q = xcd_major(blockIdx.x, gridDim.x);
+  const int g = q / s, j = q % s;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t = threadIdx.x;  // token of the per-token steps (t < 256)
+  const int64_t H = p.H, V = p.V, L = p.L;
+  const int64_t c0 = (int64_t)j * HS;
+  const rsrc_t park = make_rsrc(p.park + (int64_t)blockIdx.x * (kParkPerWG / 4), kPark ? kParkPerWG : 0);
+  const int64_t slot_elems = (int64_t)s * 256 * 256;
+  // this group's statistics exchange: [2][s][256] round maxima, [s][256] sums
+  const rsrc_t rstat = make_rsrc(p.xstat + (int64_t)g * 3 * s * 256, (uint64_t)3 * s * 256 * 4);
+  const int vt256 = (int)((V + 255) / 256);
+  const int vt128 = (int)((V + 127) / 128);
+  const int rounds = (vt256 + s - 1) / s;
+  const int nrb = (int)((L + 255) / 256);
+  unsigned epoch = 0, nbar = 0;
+
+  for (int rb = g; rb < nrb; rb += p.n_groups) {
+    const int64_t r0 = (int64_t)rb * 256;
+    const int64_t rend = min(r0 + 256, L);
+    const Operand oh = linear_operand(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
+    if (t < 256) row_m[t] = -INFINITY;  // ordered by the barriers below
+    float ssum[4] = {0.f, 0.f, 0.f, 0.f};  // lane's sums of exp(z - M) for its 4 tokens
+    f32x16 dacc[C::MB][C::NB];
+    if constexpr (!kPark) zero_acc(dacc);
+    for (int k = 0; k < rounds; ++k, ++epoch) {
+      u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
+      const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
+      const uint32_t xm = (uint32_t)((k & 1) * s * 256 * 4);  // this round's maxima slot (bytes)
+      const int vt = k * s + j;
+      const bool produce = vt < vt256;
+      float psum[4] = {0.f, 0.f, 0.f, 0.f};  // lane's sums of exp(z - m_j)
+      if (produce) {
+        const int v0 = vt * 256;
+        const int vlim = min((int)(V - v0), 256);
+        f32x16 z[P::MB][P::NB];
+        zero_acc(z);
+        P::run(linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2)), oh, (int)H, lds,
+               z);
+        // per-token maximum of the tile: the lane's 32 values, the other lane
+        // half, then the 4 waves that share the token
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int vl0 = wm * 64 + mb * 32 + acc_row(qq * 4, lane);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) mx = (vl0 + e < vlim) ? fmaxf(mx, z[mb][nb][qq * 4 + e]) : mx;
+            }
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          if (lane < 32) red[wm][wn * 128 + nb * 32 + lane] = mx;
+        }
+        __syncthreads();  // also: every wave is done with the GEMM's LDS stages
+        if (t < 256) row_l[t] = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+        __syncthreads();
+        // P_j = exp(z - m_j), staged in LDS as [token][v]; columns past V are 0
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const float ml = row_l[wn * 128 + nb * 32 + (lane & 31)] * kLog2e;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              float gv[4];
+              const int vl0 = wm * 64 + mb * 32 + acc_row(qq * 4, lane);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float pr = exp2_fast(__builtin_fmaf(z[mb][nb][qq * 4 + e], kLog2e, -ml));
+                gv[e] = (vl0 + e < vlim) ? pr : 0.f;
+                psum[nb] += gv[e];
+              }
+              gstage_put(lds, wn * 128 + nb * 32 + (lane & 31), vl0, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else if (t < 256) {
+        row_l[t] = -INFINITY;
+      }
+      if (t < 256) store_sc1_b32(rstat, (uint32_t)t * 4u, xm + (uint32_t)j * 1024u, row_l[t]);
+      if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (++nbar), p.spin_limit, p.hdr, &s_flag)) return;
+      if (t < 256) {
+        const float old = row_m[t];
+        float mx = old;
+        for (int i = 0; i < s; ++i) mx = fmaxf(mx, load_sc1_b32(rstat, (uint32_t)t * 4u, xm + (uint32_t)i * 1024u));
+        row_a[t] = (old == -INFINITY) ? 0.f : exp2_fast((old - mx) * kLog2e);
+        row_f[t] = (row_l[t] == -INFINITY) ? 0.f : exp2_fast((row_l[t] - mx) * kLog2e);
+        row_m[t] = mx;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int tok = wn * 128 + nb * 32 + (lane & 31);
+        ssum[nb] = __builtin_fmaf(ssum[nb], row_a[tok], psum[nb] * row_f[tok]);
+      }
+      if (produce) gstage_flush_scaled(lds, row_f, rslot, j);
       if constexpr (kPark) {
-        if (k + 1 < rounds) park_acc(dacc, park, wave, lane);
+        if (k == 0) zero_acc(dacc);
+        else unpark_acc(dacc, park, wave, lane);
+      }
+      if (k > 0) {
+        // O rows (tokens) follow the new maximum
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int reg = 0; reg < 16; ++reg) {
+            const float a = row_a[wm * 64 + mb * 32 + acc_row(reg, lane)];
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) dacc[mb][nb][reg] *= a;
+          }
+      }
+      if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (++nbar), p.spin_limit, p.hdr, &s_flag)) return;
+      const int ntl = min(2 * s, vt128 - k * 2 * s);
+      const int64_t vbase = (int64_t)k * s * 256;
+      C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
+             tiled_operand(p.WT + (vbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
+             lds, dacc);
+      if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
+    }
+    // row sums: lane halves, the 4 waves, then the s members
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const float v = ssum[nb] + __shfl_xor(ssum[nb], 32);
+      if (lane < 32) red[wm][wn * 128 + nb * 32 + lane] = v;
+    }
+    __syncthreads();
+    if (t < 256)
+      store_sc1_b32(rstat, (uint32_t)t * 4u, (uint32_t)(2 * s * 1024 + j * 1024),
+                    (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]));
+    if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (++nbar), p.spin_limit, p.hdr, &s_flag)) return;
+    if (t < 256) {
+      float sum = 0.f;
+      for (int i = 0; i < s; ++i) sum += load_sc1_b32(rstat, (uint32_t)t * 4u, (uint32_t)(2 * s * 1024 + i * 1024));
+      row_a[t] = 1.f / sum;
+      if (j == 0 && r0 + t < L) {
+        p.part_m[r0 + t] = row_m[t];
+        p.part_s[r0 + t] = sum;
       }
     }
-    store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
+    __syncthreads();
+    f32x16 fin[C::MB][C::NB];
+    if constexpr (kPark) unpark_acc(fin, park, wave, lane);
+    else {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) fin[mb][nb] = dacc[mb][nb];
+    }
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int reg = 0; reg < 16; ++reg) {
+        const float a = row_a[wm * 64 + mb * 32 + acc_row(reg, lane)];
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) fin[mb][nb][reg] *= a;
+      }
+    store_tile_f32(p.O + r0 * H + c0, L - r0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
+  }
+}
+
+// dh = g/N * (O - W_y) for rows with a label, 0 for the others; NaN (and the
+// state flag) if the workspace does not hold a training forward's O.
+__global__ __launch_bounds__(256) void k_dh_finish(BwdArgs p) {
+  const int64_t r = blockIdx.x;
+  const int64_t H = p.H;
+  const int64_t y = p.labels[r];
+  const bool valid = y != p.ignore_index && y >= 0 && y < p.V;
+  const bool ok = p.hdr->saved == kSavedTag;
+  const int n = p.hdr->n_valid;
+  const float scale = *p.grad_loss / (float)(n > 0 ? n : 1);
+  if (!ok && r == 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_or(&p.hdr->status, kStatusState, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float4* o = reinterpret_cast<const float4*>(p.O + r * H);
+  const u16* w = p.W + (valid ? y : 0) * H;
+  float4* d = reinterpret_cast<float4*>(p.dh + r * H);
+  for (int64_t c = threadIdx.x; c < H / 4; c += 256) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!ok) {
+      v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+    } else if (valid) {
+      const float4 ov = o[c];
+      const bf16x4 wv = *reinterpret_cast<const bf16x4*>(w + c * 4);
+      v = make_float4(scale * (ov.x - (float)wv[0]), scale * (ov.y - (float)wv[1]), scale * (ov.z - (float)wv[2]),
+                      scale * (ov.w - (float)wv[3]));
+    }
+    d[c] = v;
   }
 }
 
@@ -406,13 +655,17 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
-const void* bwd_kernel(bool dh, int hs) {
-  if (hs == 256)
-    return dh ? reinterpret_cast<const void*>(&k_bwd_dh<256>) : reinterpret_cast<const void*>(&k_bwd_dW<256>);
-  return dh ? reinterpret_cast<const void*>(&k_bwd_dh<128>) : reinterpret_cast<const void*>(&k_bwd_dW<128>);
+const void* bwd_kernel(int pass, int hs) {
+  if (hs == 256 && pass != kPassFwdDh) {
+    if (pass == kPassDh) return reinterpret_cast<const void*>(&k_bwd_dh<256>);
+    return reinterpret_cast<const void*>(&k_bwd_dW<256>);
+  }
+  if (pass == kPassDh) return reinterpret_cast<const void*>(&k_bwd_dh<128>);
+  if (pass == kPassDw) return reinterpret_cast<const void*>(&k_bwd_dW<128>);
+  return reinterpret_cast<const void*>(&k_fwd_dh<128>);
 }
 
-hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs) {
+hipError_t bwd_resident_wgs(int pass, int hs, int* wgs) {
   int dev = 0, cus = 0, per = 0, coop = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -421,16 +674,21 @@ hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs) {
   e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
   if (e != hipSuccess) return e;
   if (!coop) return hipErrorNotSupported;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_kernel(dh, hs), kBwdThreads, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_kernel(pass, hs), kBwdThreads, 0);
   if (e != hipSuccess) return e;
   *wgs = cus * per;
   return hipSuccess;
 }
 
-hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int hs, int n_wgs, hipStream_t st) {
+hipError_t launch_bwd_group(int pass, const BwdArgs& a, int hs, int n_wgs, hipStream_t st) {
   BwdArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchCooperativeKernel(bwd_kernel(dh, hs), dim3((unsigned)n_wgs), dim3(kBwdThreads), args, 0, st);
+  return hipLaunchCooperativeKernel(bwd_kernel(pass, hs), dim3((unsigned)n_wgs), dim3(kBwdThreads), args, 0, st);
+}
+
+hipError_t launch_dh_finish(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_dh_finish, dim3((unsigned)a.L), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace lmce

@@ -322,6 +322,14 @@ __device__ __forceinline__ void store_sc1_b128(rsrc_t rs, uint32_t voff, uint32_
   __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, soff, kAuxSc1);
 }
 
+// 4-byte buffer store and load, coherent at device scope.
+__device__ __forceinline__ void store_sc1_b32(rsrc_t rs, uint32_t voff, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, soff, kAuxSc1);
+}
+__device__ __forceinline__ float load_sc1_b32(rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kAuxSc1));
+}
+
 // 4-byte buffer store (stores past the resource end are dropped).
 __device__ __forceinline__ void store_b32(rsrc_t rs, uint32_t voff, uint32_t soff, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, voff, soff, 0);

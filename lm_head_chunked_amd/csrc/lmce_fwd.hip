@@ -19,8 +19,9 @@ namespace lmce {
 
 // Counts rows whose label is not ignore_index and checks that the others lie
 // in [0, V).  One workgroup; fixed-order reduction.
+// `saved` >= 0 is written to the header's training-forward tag.
 __global__ __launch_bounds__(1024) void k_count_labels(const int64_t* __restrict__ labels, int64_t L, int64_t V,
-                                                       int64_t ignore_index, WsHeader* __restrict__ hdr) {
+                                                       int64_t ignore_index, WsHeader* __restrict__ hdr, int saved) {
   __shared__ int s_cnt[1024];
   __shared__ int s_bad[1024];
   int cnt = 0, bad = 0;
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(1024) void k_count_labels(const int64_t* __restrict
   if (threadIdx.x == 0) {
     hdr->n_valid = s_cnt[0];
     hdr->status = s_bad[0] ? kStatusLabel : 0;
+    if (saved >= 0) hdr->saved = saved;
   }
 }
 
@@ -245,8 +247,8 @@ __global__ __launch_bounds__(256) void k_fwd_loss(FwdArgs p, int nblocks, float*
 }
 
 hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int64_t ignore_index, WsHeader* hdr,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(k_count_labels, dim3(1), dim3(1024), 0, st, labels, L, V, ignore_index, hdr);
+                               int saved, hipStream_t st) {
+  hipLaunchKernelGGL(k_count_labels, dim3(1), dim3(1024), 0, st, labels, L, V, ignore_index, hdr, saved);
   return hipGetLastError();
 }
 
@@ -256,6 +258,13 @@ hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStre
   else hipLaunchKernelGGL(k_fwd<128>, dim3(items), dim3(kFwdThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_fwd_rows(a, loss_out, lse_out, st);
+}
+
+// Merges the per-segment (max, sum) partials of every row into lse, forms
+// nll and the loss.
+hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st) {
+  hipError_t e;
   const int nblocks = (int)((a.L + 63) / 64);
   hipLaunchKernelGGL(k_fwd_rows, dim3(nblocks), dim3(256), 0, st, a, lse_out);
   e = hipGetLastError();

@@ -9,18 +9,22 @@ namespace lmce {
 
 constexpr int kStatusLabel = 1;     // asynchronous flag: a label was out of range
 constexpr int kStatusSync = 2;      // asynchronous flag: a group wait timed out
+constexpr int kStatusState = 4;     // asynchronous flag: a training backward without its training forward
+constexpr int kSavedTag = 0x6c6d6365;  // header tag: the workspace holds a training forward's O
 constexpr int kStageK = 128;        // hidden-size granularity (the backward slices H by 128)
 constexpr int kVTile = 256;         // vocabulary rows per forward logit tile
 constexpr int kSyncStride = 64;     // u32 words between two groups' counters (256 bytes)
 constexpr int kMaxBwdWGs = 256;     // upper bound of a backward cooperative grid
 constexpr int kXbufPerWG = 2 * 256 * 256 * 2;  // exchange bytes per backward workgroup (2 slots x one 256 x 256 bf16 tile)
 constexpr int kParkPerWG = 256 * 256 * 4;      // parked 256 x 256 fp32 accumulator slice per backward workgroup
+constexpr int kXstatPerWG = 3 * 256 * 4;       // fused forward: per-member round maxima (2 slots) and final sums
 
 // First 256 bytes of the workspace.
 struct WsHeader {
   int n_valid;   // rows whose label is not ignore_index (and is in range)
-  int status;    // 0, or kStatusLabel | kStatusSync
-  int pad[62];
+  int status;    // 0, or kStatusLabel | kStatusSync | kStatusState
+  int saved;     // kSavedTag once a training forward has filled O, else 0
+  int pad[61];
 };
 
 struct FwdArgs {
@@ -57,17 +61,25 @@ struct BwdArgs {
   unsigned* sync;       // [n_groups * kSyncStride] arrival counters, zeroed before the launch
   uint16_t* xbuf;       // [n_groups][2][2 * group_size][256][128] exchange slots
   float* park;          // [workgroups][256 x 256] parked accumulators (HS = 256 only)
+  float* xstat;         // [n_groups][3][group_size][256] round maxima (2 slots) and final sums, fused forward
+  float* O;             // [L][H] normalised sum_v softmax(z)_v W_v, fused forward output
+  float* part_m;        // [L] row max, fused forward output
+  float* part_s;        // [L] row sum of exp(z - max), fused forward output
   WsHeader* hdr;
   float* dh;
   float* dW;
 };
 
 hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int64_t ignore_index, WsHeader* hdr,
-                               hipStream_t st);
+                               int saved, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
+hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
 hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
-hipError_t bwd_resident_wgs(bool dh, int hs, int* wgs);
-hipError_t launch_bwd_group(bool dh, const BwdArgs& a, int hs, int n_wgs, hipStream_t st);
+// Group-scheduled kernels: the two backward passes and the fused training forward.
+constexpr int kPassDh = 0, kPassDw = 1, kPassFwdDh = 2;
+hipError_t bwd_resident_wgs(int pass, int hs, int* wgs);
+hipError_t launch_bwd_group(int pass, const BwdArgs& a, int hs, int n_wgs, hipStream_t st);
+hipError_t launch_dh_finish(const BwdArgs& a, hipStream_t st);
 
 }  // namespace lmce

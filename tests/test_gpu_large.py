@@ -52,15 +52,22 @@ def label_logits_fp64(h, W, y, block=8192):
     return out
 
 
+def pair(train):
+    """The plain pair, or the training pair that bench.py times."""
+    return (lm.lmce_fwd_train, lm.lmce_bwd_train) if train else (lm.lmce_fwd, lm.lmce_bwd)
+
+
+@pytest.mark.parametrize("train", [False, True], ids=["plain", "train"])
 @pytest.mark.parametrize("name", LARGE)
-def test_full_size_sampled_parity(name):
+def test_full_size_sampled_parity(name, train):
     wl = synth.WORKLOADS[name]
-    say(f"[case] {name} full size L={wl.L} H={wl.H} V={wl.V}")
+    say(f"[case] {name} full size L={wl.L} H={wl.H} V={wl.V} train={train}")
     dev = torch.device("cuda:0")
     h, W, y = synth.make(wl, device=dev)
     ws = torch.empty(lm.lmce_workspace_size(wl.L, wl.H, wl.V, 256), dtype=torch.uint8, device=dev)
-    loss, lse = lm.lmce_fwd(h, W, y, -100, 256, ws)
-    dh, dW = lm.lmce_bwd(h, W, y, lse, None, -100, 256, ws)
+    fwd, bwd = pair(train)
+    loss, lse = fwd(h, W, y, -100, 256, ws)
+    dh, dW = bwd(h, W, y, lse, None, -100, 256, ws)
     assert lm.lmce_read_status(ws) == _lib.LMCE_OK
     torch.cuda.synchronize()
     say(f"[{name}] gpu done, loss {float(loss):.6f}")
@@ -101,18 +108,20 @@ def test_full_size_sampled_parity(name):
     del dh, dW, ws
 
 
+@pytest.mark.parametrize("train", [False, True], ids=["plain", "train"])
 @pytest.mark.parametrize("name", LARGE)
-def test_reduced_rows_full_parity(name):
+def test_reduced_rows_full_parity(name, train):
     wl = synth.WORKLOADS[name]
     Lr = 1024
-    say(f"[case] {name} first {Lr} rows at H={wl.H} V={wl.V} (oracle ~20-60 s)")
+    say(f"[case] {name} first {Lr} rows at H={wl.H} V={wl.V} train={train} (oracle ~5-20 s)")
     dev = torch.device("cuda:0")
     h, W, y = synth.make(wl, device=dev)
     h = h[:Lr].contiguous()
     y = y[:Lr].contiguous()
     ws = torch.empty(lm.lmce_workspace_size(Lr, wl.H, wl.V, 256), dtype=torch.uint8, device=dev)
-    loss, lse = lm.lmce_fwd(h, W, y, -100, 256, ws)
-    dh, dW = lm.lmce_bwd(h, W, y, lse, None, -100, 256, ws)
+    fwd, bwd = pair(train)
+    loss, lse = fwd(h, W, y, -100, 256, ws)
+    dh, dW = bwd(h, W, y, lse, None, -100, 256, ws)
     torch.cuda.synchronize()
     ref = oracle.fwd_bwd(np32(h), np32(W), y.cpu().numpy())
     e = (abs(float(loss) - ref["loss"]) / abs(ref["loss"]), float(np.max(np.abs(lse.cpu().numpy() - ref["lse"]))),

@@ -37,15 +37,17 @@ def rel_fro(a, b):
     return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
 
 
-def run_gpu(h, W, y, chunk_rows=256, grad=1.0, ignore_index=-100):
+def run_gpu(h, W, y, chunk_rows=256, grad=1.0, ignore_index=-100, train=False):
+    """lmce_fwd + lmce_bwd, or (train=True) the training pair lmce_fwd_train + lmce_bwd_train."""
     dev = torch.device("cuda:0")
     h_d, W_d, y_d = h.to(dev), W.to(dev), y.to(dev)
     L, H = h.shape
     V = W.shape[0]
     ws = torch.empty(lm.lmce_workspace_size(L, H, V, chunk_rows), dtype=torch.uint8, device=dev)
-    loss, lse = lm.lmce_fwd(h_d, W_d, y_d, ignore_index, chunk_rows, ws)
+    fwd, bwd = (lm.lmce_fwd_train, lm.lmce_bwd_train) if train else (lm.lmce_fwd, lm.lmce_bwd)
+    loss, lse = fwd(h_d, W_d, y_d, ignore_index, chunk_rows, ws)
     g = torch.tensor(grad, dtype=torch.float32, device=dev)
-    dh, dW = lm.lmce_bwd(h_d, W_d, y_d, lse, g, ignore_index, chunk_rows, ws)
+    dh, dW = bwd(h_d, W_d, y_d, lse, g, ignore_index, chunk_rows, ws)
     status = lm.lmce_read_status(ws)
     torch.cuda.synchronize()
     return {"loss": float(loss), "lse": lse.cpu().numpy(), "dh": dh.cpu().numpy(), "dW": dW.cpu().numpy(),
@@ -119,6 +121,67 @@ def test_wide_slices(L, H, V, ign):
     assert_parity(gpu, ref, f"L={L} H={H} V={V}")
     ign_rows = (y == -100).numpy()
     assert np.all(gpu["dh"][ign_rows] == 0.0)
+
+
+# The training pair: one vocabulary sweep gives lse and O = sum_v softmax W_v;
+# dh = g/N (O - W_y).  Same bar against the oracle, over the same edge cases.
+TRAIN = [
+    (512, 256, 4096, 0.1),
+    (300, 128, 700, 0.2),
+    (1, 128, 1, 0.0),
+    (77, 128, 4097, 0.5),
+    (513, 640, 2000, 0.3),
+    (1000, 512, 130, 0.05),
+    (5500, 3072, 2500, 0.1),
+    (600, 3072, 5500, 0.1),
+]
+
+
+@pytest.mark.parametrize("L,H,V,ign", TRAIN)
+def test_train_pair_parity(L, H, V, ign):
+    say(f"[case] train pair L={L} H={H} V={V} ignore={ign}")
+    h, W, y = synth.random_case(L, H, V, seed=L + V + 1, w_std=0.05, ignore_frac=ign)
+    gpu = run_gpu(h, W, y, chunk_rows=256, grad=1.5, train=True)
+    ref = oracle.fwd_bwd(np32(h), np32(W), y.numpy(), grad=1.5)
+    if ref["n_valid"] == 0 or abs(ref["loss"]) < 1e-6:
+        assert np.max(np.abs(gpu["lse"] - ref["lse"])) <= LSE_ABS
+        return
+    assert_parity(gpu, ref, f"train L={L} H={H} V={V}")
+    ign_rows = (y == -100).numpy()
+    assert np.all(gpu["dh"][ign_rows] == 0.0)
+
+
+def test_train_pair_matches_plain_pair_and_is_deterministic():
+    say("[case] train pair vs plain pair, qwen3_0.6b head")
+    h, W, y = synth.make("qwen3_0.6b")
+    a = run_gpu(h, W, y, train=True)
+    b = run_gpu(h, W, y, train=True)
+    c = run_gpu(h, W, y, train=False)
+    for k in ("lse", "dh", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["loss"] == b["loss"]
+    assert abs(a["loss"] - c["loss"]) <= 1e-5 * abs(c["loss"])
+    assert np.max(np.abs(a["lse"] - c["lse"])) <= 1e-4
+    assert rel_fro(a["dh"], c["dh"]) <= 5e-3
+    # the same dW pass, fed the fused forward's lse (equal up to rounding)
+    assert rel_fro(a["dW"], c["dW"]) <= 1e-3
+
+
+def test_train_backward_without_train_forward_is_reported():
+    say("[case] lmce_bwd_train after a plain lmce_fwd")
+    h, W, y = synth.random_case(256, 128, 600, seed=11)
+    dev = torch.device("cuda:0")
+    hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
+    ws = torch.empty(lm.lmce_workspace_size(256, 128, 600), dtype=torch.uint8, device=dev)
+    loss, lse = lm.lmce_fwd(hd, Wd, yd, workspace=ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws)
+    assert lm.lmce_read_status(ws) == _lib.LMCE_ERR_STATE
+    assert torch.isnan(dh).all()
+    # a training forward on the same workspace makes the pair valid again
+    loss, lse = lm.lmce_fwd_train(hd, Wd, yd, workspace=ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws)
+    assert lm.lmce_read_status(ws) == _lib.LMCE_OK
+    assert torch.isfinite(dh).all()
 
 
 def test_results_do_not_depend_on_chunk_rows():
