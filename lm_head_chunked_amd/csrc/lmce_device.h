@@ -87,26 +87,30 @@ __device__ __forceinline__ void raw_barrier() {
 }
 
 // ------------------------------------------------------------------ stages
-// A pipeline stage holds ROWS rows x 32 bf16 (64 bytes = four 16-byte chunks
-// per row).  Logical chunk c of row r sits in physical slot c ^ swz(r), which
-// spreads the eight (32-bank) or sixteen (64-bank) rows read together by a
-// ds_read_b128 over distinct banks.
-__device__ __forceinline__ int swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
+// A pipeline stage holds ROWS rows x 64 bf16 (128 bytes = eight 16-byte
+// chunks per row, one whole cache line).  Logical chunk c of row r sits in
+// physical slot c ^ swz(r).  Over every 8 consecutive rows that start at a
+// multiple of 8, swz is a permutation of 0..7, and so it is over the even and
+// over the odd rows of every 16 such rows: the rows that a ds_read_b128
+// serves together (one chunk of consecutive rows) hit distinct banks with
+// either a 32- or a 64-bank LDS.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
 // One wave-level LDS-DMA load moves 1 KiB: lane i lands at lds_base + 16*i,
-// i.e. rows r0 .. r0+15, physical slot i % 4.  The NW waves of the
-// workgroup issue ROWS/16/NW of them each.
+// i.e. rows r0 .. r0+7, physical slot i % 8, so the eight lanes of a row
+// read its whole 128-byte line.  The NW waves of the workgroup issue
+// ROWS/8/NW of them each.
 template <int ROWS, int NW, int AUX>
 __device__ __forceinline__ void stage_dma(rsrc_t rs, uint32_t ld_bytes, uint32_t col_bytes, char* region, int wave,
                                           int lane) {
-  static_assert(ROWS % (16 * NW) == 0, "rows per stage must split evenly over the waves");
+  static_assert(ROWS % (8 * NW) == 0, "rows per stage must split evenly over the waves");
 #pragma unroll
-  for (int q = 0; q < ROWS / 16 / NW; ++q) {
-    const int r0 = (wave * (ROWS / 16 / NW) + q) * 16;
-    const int r = r0 + (lane >> 2);
-    const int c = (lane & 3) ^ swz(r);
+  for (int q = 0; q < ROWS / 8 / NW; ++q) {
+    const int r0 = (wave * (ROWS / 8 / NW) + q) * 8;
+    const int r = r0 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
     const uint32_t voff = (uint32_t)r * ld_bytes + col_bytes + (uint32_t)c * 16u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LMCE_LDS_PTR(region + r0 * 64), 16, voff, 0, 0, AUX);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LMCE_LDS_PTR(region + r0 * 128), 16, voff, 0, 0, AUX);
   }
 }
 
@@ -115,7 +119,7 @@ __device__ __forceinline__ void stage_dma(rsrc_t rs, uint32_t ld_bytes, uint32_t
 // read and serialise the prefetch pipeline.  The caller waits for the reads
 // with lds_wait_frags() before using the fragments.
 __device__ __forceinline__ bf16x8 stage_frag(const char* region, int row, int chunk) {
-  const char* p = region + (row * 4 + (chunk ^ swz(row))) * 16;
+  const char* p = region + (row * 8 + (chunk ^ swz(row))) * 16;
   const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
   bf16x8 v;
   asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
@@ -164,8 +168,11 @@ __device__ __forceinline__ void lds_wait_frags(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB
 // acc[mb][nb] += sum_k A[m][k] * B[n][k] over a BM x BN tile, WM x WN waves,
 // each wave (wm, wn) owning rows wm*BM/WM + mb*32 + acc_row(.) and columns
 // wn*BN/WN + nb*32 + lane%32.  A and B are bf16 with K contiguous,
-// reached through buffer resources.  K % 32 == 0.  Four LDS stages are kept
-// in flight by LDS-DMA loads; one barrier per 32-wide K step.
+// reached through buffer resources.  K % 64 == 0.  LDS-DMA loads keep the
+// next stages in flight (two 64 KiB stages of a 256 x 256 tile, three 48 KiB
+// stages of a 256 x 128 one); one barrier per 64-wide K step.  Whole-line
+// (128-byte) row segments per stage matter on gfx950: with 64-byte segments
+// the same tiles ran 10 % (256 x 256) and 25 % (256 x 128) slower.
 //
 // Operand addressing (bytes from the resource base): row r, K index k is at
 //   linear  (KT == 0):  r * ld + col + 2k
@@ -180,27 +187,29 @@ struct Operand {
 
 template <int KT>
 __device__ __forceinline__ uint32_t k_offset(const Operand& o, int kt) {
-  if constexpr (KT == 0) return o.col + (uint32_t)kt * 64u;
-  else return (uint32_t)(kt >> 2) * o.tstride + (uint32_t)(kt & 3) * 64u;
+  if constexpr (KT == 0) return o.col + (uint32_t)kt * 128u;
+  else return (uint32_t)(kt >> 1) * o.tstride + (uint32_t)(kt & 1) * 128u;
 }
 
 template <int BM, int BN, int WM, int WN, int AUXA = 0, int KTA = 0, int KTB = 0, bool PF = false>
 struct TileGemm {
   static constexpr int NW = WM * WN;             // waves
   static constexpr int NT = 64 * NW;             // threads
-  static constexpr int BK = 32;
-  static constexpr int STAGES = 4;
+  static constexpr int BK = 64;
+  static constexpr int NKS = BK / 16;            // MFMA K sub-steps per stage
+  static constexpr int STAGES = BM + BN <= 384 ? 3 : 2;
   static constexpr int MB = BM / WM / 32;        // 32-row blocks per wave
   static constexpr int NB = BN / WN / 32;        // 32-column blocks per wave
-  static constexpr int LOADS = (BM + BN) / 16 / NW;  // DMA instructions per wave per stage
-  static constexpr int STAGE_BYTES = (BM + BN) * 64;
+  static constexpr int LOADS = (BM + BN) / 8 / NW;  // DMA instructions per wave per stage
+  static constexpr int STAGE_BYTES = (BM + BN) * 128;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(LDS_BYTES <= 144 * 1024, "leave LDS for the kernels' own arrays");
 
   __device__ __forceinline__ static void issue(int kt, const Operand& a, const Operand& b, char* lds, int wave,
                                                int lane) {
     char* st = lds + (kt % STAGES) * STAGE_BYTES;
     stage_dma<BM, NW, AUXA>(a.rs, a.ld, k_offset<KTA>(a, kt), st, wave, lane);
-    stage_dma<BN, NW, 0>(b.rs, b.ld, k_offset<KTB>(b, kt), st + BM * 64, wave, lane);
+    stage_dma<BN, NW, 0>(b.rs, b.ld, k_offset<KTB>(b, kt), st + BM * 128, wave, lane);
   }
 
   __device__ __forceinline__ static void run(const Operand& a, const Operand& b, int K, char* lds,
@@ -219,40 +228,49 @@ struct TileGemm {
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < nk) issue(s, a, b, lds, wave, lane);
     for (int kt = 0; kt < nk; ++kt) {
-      const int later = nk - 1 - kt;  // stages issued after kt (capped at STAGES - 2)
-      if (later >= 2) wait_vmcnt<2 * LOADS>();
-      else if (later == 1) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
+      // stage kt has landed (with three stages, kt + 1 may still be in flight)
+      if constexpr (STAGES == 3) {
+        if (kt + 1 < nk) wait_vmcnt<LOADS>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
       raw_barrier();
+      // the stage refilled here was last read in step kt - 1, whose reads
+      // every wave completed before the barrier
       if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, a, b, lds, wave, lane);
       const char* sa = lds + (kt % STAGES) * STAGE_BYTES;
-      const char* sb = sa + BM * 64;
+      const char* sb = sa + BM * 128;
       if constexpr (PF) {
-        // both 16-wide K sub-steps' fragments up front: the second half's
-        // reads complete while the first half's MFMAs run
-        bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
-        const int ca = lane >> 5, cb = 2 + (lane >> 5);
+        // the next sub-step's fragments are read while this one's MFMAs run
+        bf16x8 fa[2][MB], fb[2][NB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) fa0[mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), ca);
+        for (int mb = 0; mb < MB; ++mb) fa[0][mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), lane >> 5);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fb0[nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), ca);
+        for (int nb = 0; nb < NB; ++nb) fb[0][nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), lane >> 5);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) fa1[mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), cb);
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int cur = ks & 1;
+          if (ks + 1 < NKS) {
+            const int c = 2 * (ks + 1) + (lane >> 5);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fb1[nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), cb);
-        lds_wait_frags_n<MB + NB>(fa0, fb0);
+            for (int mb = 0; mb < MB; ++mb)
+              fa[cur ^ 1][mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), c);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+            for (int nb = 0; nb < NB; ++nb)
+              fb[cur ^ 1][nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), c);
+            lds_wait_frags_n<MB + NB>(fa[cur], fb[cur]);
+          } else {
+            lds_wait_frags_n<0>(fa[cur], fb[cur]);
+          }
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa0[mb], fb0[nb], acc[mb][nb]);
-        lds_wait_frags_n<0>(fa1, fb1);
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa1[mb], fb1[nb], acc[mb][nb]);
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa[cur][mb], fb[cur][nb], acc[mb][nb]);
+        }
       } else {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
           const int c = 2 * ks + (lane >> 5);
           bf16x8 fa[MB], fb[NB];
 #pragma unroll
