@@ -58,11 +58,22 @@ __global__ void k_zero_u32(unsigned* __restrict__ p, int n) {
 }
 
 // Position of workgroup b in XCD-major order (workgroups are dispatched to
-// the 8 XCDs round-robin), so that the members of a group share an L2.
+// the 8 XCDs round-robin), so that the members of a group share an L2.  Used
+// by the dW pass, whose members all load their group's vocabulary tile of W.
 __device__ __forceinline__ int xcd_major(int b, int nwg) {
   if (nwg % 8 != 0) return b;
   return (b & 7) * (nwg >> 3) + (b >> 3);
 }
+
+// Position of workgroup b with the members of each group spread over the
+// XCDs: b = g * s + j, so member j of every group sits on XCD (g * s + j) % 8,
+// which is j % 8 for all groups when s is a multiple of 8.  Used by the
+// passes whose groups own row blocks: in a round, member j of every group
+// loads the same vocabulary tile of W (and the same H slice of W^T), so
+// groups that share an XCD read it through one L2 instead of each fetching
+// it from HBM or the Infinity Cache.  The exchange then crosses XCDs, which
+// its device-coherent stores and loads allow.
+__device__ __forceinline__ int member_spread(int b) { return b; }
 
 // All s members of group g have written round `epoch`; bounded wait.
 // Returns false (and records kStatusSync) if the group did not arrive.
@@ -183,7 +194,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   __shared__ int s_flag;
 
   const int s = p.group_size;
-  const int q = xcd_major(blockIdx.x, gridDim.x);
+  const int q = member_spread(blockIdx.x);
   const int g = q / s, j = q % s;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -450,7 +461,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
   __shared__ int s_flag;
 
   const int s = p.group_size;
-  const int q = xcd_major(blockIdx.x, gridDim.x);
+  const int q = member_spread(blockIdx.x);
   const int g = q / s, j = q % s;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
