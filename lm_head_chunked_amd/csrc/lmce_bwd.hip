@@ -413,6 +413,33 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
 }
 
 // ----------------------------------------------------- fused training forward
+// Maximum and sum of one value per group member (member i's value at byte
+// offset base + i * 1024 + voff of the statistics exchange).  Eight loads are
+// issued before any is used, so a round waits for s / 8 device-coherent
+// round trips instead of s.  The sum adds the members in index order.
+__device__ __forceinline__ float group_max(rsrc_t rs, int s, uint32_t voff, uint32_t base) {
+  float mx = -INFINITY;
+  for (int i0 = 0; i0 < s; i0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = i0 + u < s ? load_sc1_b32(rs, voff, base + (uint32_t)(i0 + u) * 1024u) : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mx = fmaxf(mx, v[u]);
+  }
+  return mx;
+}
+__device__ __forceinline__ float group_sum(rsrc_t rs, int s, uint32_t voff, uint32_t base) {
+  float sum = 0.f;
+  for (int i0 = 0; i0 < s; i0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = i0 + u < s ? load_sc1_b32(rs, voff, base + (uint32_t)(i0 + u) * 1024u) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  return sum;
+}
+
 // Copies the staged tile like gstage_flush, scaling row r by fac[r] on the way.
 __device__ __forceinline__ void gstage_flush_scaled(const char* lds, const float* fac, rsrc_t rslot, int j) {
   const int t = threadIdx.x;
@@ -547,8 +574,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (++nbar), p.spin_limit, p.hdr, &s_flag)) return;
       if (t < 256) {
         const float old = row_m[t];
-        float mx = old;
-        for (int i = 0; i < s; ++i) mx = fmaxf(mx, load_sc1_b32(rstat, (uint32_t)t * 4u, xm + (uint32_t)i * 1024u));
+        const float mx = fmaxf(old, group_max(rstat, s, (uint32_t)t * 4u, xm));
         row_a[t] = (old == -INFINITY) ? 0.f : exp2_fast((old - mx) * kLog2e);
         row_f[t] = (row_l[t] == -INFINITY) ? 0.f : exp2_fast((row_l[t] - mx) * kLog2e);
         row_m[t] = mx;
@@ -595,8 +621,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
                     (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]));
     if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (++nbar), p.spin_limit, p.hdr, &s_flag)) return;
     if (t < 256) {
-      float sum = 0.f;
-      for (int i = 0; i < s; ++i) sum += load_sc1_b32(rstat, (uint32_t)t * 4u, (uint32_t)(2 * s * 1024 + i * 1024));
+      const float sum = group_sum(rstat, s, (uint32_t)t * 4u, (uint32_t)(2 * s * 1024));
       row_a[t] = 1.f / sum;
       if (j == 0 && r0 + t < L) {
         p.part_m[r0 + t] = row_m[t];
