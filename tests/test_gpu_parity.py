@@ -151,6 +151,49 @@ def test_train_pair_parity(L, H, V, ign):
     assert np.all(gpu["dh"][ign_rows] == 0.0)
 
 
+def _max_jumps(z, s, jump=16.0):
+    """(jumps, flat) counts of vocabulary rounds after the first in which some
+    row's running maximum rises by more than `jump` (or by no more), on fp64
+    logits z [L, V], with rows in 256-row blocks and rounds of s 256-column
+    tiles as in the fused training forward."""
+    L, V = z.shape
+    jumps = flat = 0
+    for r0 in range(0, L, 256):
+        zb = z[r0:r0 + 256]
+        run = zb[:, :256 * s].max(axis=1)
+        for v0 in range(256 * s, V, 256 * s):
+            m = np.maximum(run, zb[:, v0:v0 + 256 * s].max(axis=1))
+            if (m > run + jump).any():
+                jumps += 1
+            else:
+                flat += 1
+            run = m
+    return jumps, flat
+
+
+def test_train_pair_parity_when_the_maximum_jumps():
+    """Logits that grow along the vocabulary, so that in later rounds of the
+    fused forward some rows' running maximum rises by more than 16 (O and the
+    row sums are then rescaled by less than exp(-16)), while in others it
+    barely moves."""
+    L, H, V = 600, 384, 6000
+    say(f"[case] train pair, growing logits L={L} H={H} V={V}")
+    h, W, y = synth.random_case(L, H, V, seed=23, w_std=0.05, ignore_frac=0.1)
+    scale = torch.ones(V)
+    scale[3000:4500] = 8.0
+    scale[4500:] = 20.0
+    W = (W.float() * scale[:, None]).to(torch.bfloat16)
+    z = np32(h).astype(np.float64) @ np32(W).astype(np.float64).T
+    jumps, flat = _max_jumps(z, H // 128)
+    assert jumps > 0 and flat > 0, (jumps, flat)
+    a = run_gpu(h, W, y, grad=1.5, train=True)
+    b = run_gpu(h, W, y, grad=1.5, train=True)
+    ref = oracle.fwd_bwd(np32(h), np32(W), y.numpy(), grad=1.5)
+    assert_parity(a, ref, f"train growing logits L={L} H={H} V={V} (jumps {jumps}, flat {flat})")
+    for k in ("lse", "dh", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+
+
 def test_train_pair_matches_plain_pair_and_is_deterministic():
     say("[case] train pair vs plain pair, qwen3_0.6b head")
     h, W, y = synth.make("qwen3_0.6b")
