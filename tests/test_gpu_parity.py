@@ -194,6 +194,38 @@ def test_train_pair_parity_when_the_maximum_jumps():
         assert np.array_equal(a[k], b[k]), k
 
 
+def _random_shapes(n, seed=2024):
+    """Seeded (L, H, V, ignore fraction, chunk_rows) draws: ragged L and V,
+    H a multiple of 128 up to 4096 (so the 256-wide slices appear too), and
+    every allowed kind of chunk_rows; sized for an fp64 oracle in seconds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        H = int(rng.choice([128, 256, 384, 640, 1024, 1536, 3072, 4096]))
+        L = int(rng.integers(1, 3000))
+        V = int(rng.integers(1, 9000))
+        if L * V * H > 2.5e10:
+            continue
+        out.append((L, H, V, float(rng.choice([0.0, 0.05, 0.3, 0.9])), int(rng.integers(1, 33)) * 32))
+    return out
+
+
+@pytest.mark.parametrize("L,H,V,ign,chunk", _random_shapes(10))
+def test_random_shapes_both_pairs(L, H, V, ign, chunk):
+    say(f"[case] random shape L={L} H={H} V={V} ignore={ign} chunk_rows={chunk}")
+    h, W, y = synth.random_case(L, H, V, seed=L * 7 + V, w_std=0.05, ignore_frac=ign)
+    ref = oracle.fwd_bwd(np32(h), np32(W), y.numpy(), grad=0.75)
+    for train in (False, True):
+        gpu = run_gpu(h, W, y, chunk_rows=chunk, grad=0.75, train=train)
+        if ref["n_valid"] == 0:
+            assert math.isnan(gpu["loss"])
+            assert np.max(np.abs(gpu["lse"] - ref["lse"])) <= LSE_ABS
+            assert not gpu["dh"].any() and not gpu["dW"].any()
+            continue
+        assert_parity(gpu, ref, f"random L={L} H={H} V={V} train={train}")
+        assert np.all(gpu["dh"][(y == -100).numpy()] == 0.0)
+
+
 def test_train_pair_matches_plain_pair_and_is_deterministic():
     say("[case] train pair vs plain pair, qwen3_0.6b head")
     h, W, y = synth.make("qwen3_0.6b")
