@@ -170,6 +170,27 @@ extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int
 
 namespace {
 
+// Members of one dW group per XCD.  In a round, the workgroups of one XCD
+// that host `a` members of each of b = nwg / 8 / a groups read a distinct h
+// blocks and h^T slices and b distinct W tiles and exchange slots, each
+// through one L2, so the XCD fetches about 4 (a + b) tile-sized operands per
+// round: the valid a with the smallest a + b is taken (on the 8B head shape,
+// a = 8 cut the pass from 313 to 293 ms against a = 16, the whole group on
+// one XCD).  0 (whole groups per XCD, xcd_major) when no a is valid.
+int dw_xcd_members(int s, int nwg) {
+  if (nwg % 8 != 0) return 0;
+  int best = 0, cost = 1 << 30;
+  for (int a = s; a >= 1; --a) {
+    if (s % a != 0 || 8 % (s / a) != 0 || (nwg / 8) % a != 0) continue;
+    const int c = a + (nwg / 8) / a;
+    if (c < cost) {
+      cost = c;
+      best = a;
+    }
+  }
+  return best;
+}
+
 // One group-scheduled pass over `items` blocks (row blocks or vocabulary
 // blocks): picks the H slice width, sizes the cooperative grid to the
 // resident workgroups, resets the group counters and launches.
@@ -195,6 +216,7 @@ int launch_group_pass(int pass, BwdArgs& a, const Plan& p, int64_t items, hipStr
   if (groups < 1) return LMCE_ERR_UNSUPPORTED;
   a.group_size = group_size;
   a.n_groups = (int)groups;
+  a.xcd_members = pass == kPassDw ? dw_xcd_members(group_size, (int)groups * group_size) : 0;
   if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
   if (launch_bwd_group(pass, a, hs, (int)groups * group_size, s) != hipSuccess) return LMCE_ERR_HIP;
   return LMCE_OK;

@@ -75,6 +75,20 @@ __device__ __forceinline__ int xcd_major(int b, int nwg) {
 // its device-coherent stores and loads allow.
 __device__ __forceinline__ int member_spread(int b) { return b; }
 
+// Position of workgroup b when every XCD hosts `a` members of each of
+// nwg / 8 / a groups: a group spans s / a XCDs, and in a round the workgroups
+// of one XCD read a distinct member operands and nwg / 8 / a distinct group
+// operands, each through one L2 (XCD x, index i on it: group
+// (x / (s/a)) * (nwg/8/a) + i / a, member (x % (s/a)) * a + i % a).  The host
+// passes a > 0 only when nwg % 8 == 0, s % a == 0, 8 % (s / a) == 0 and
+// (nwg / 8) % a == 0; the map is then a bijection of [0, nwg).
+__device__ __forceinline__ int xcd_tiled(int b, int nwg, int s, int a) {
+  const int x = b & 7, i = b >> 3;
+  const int per = s / a;
+  const int bg = (nwg >> 3) / a;
+  return ((x / per) * bg + i / a) * s + (x % per) * a + i % a;
+}
+
 // All s members of group g have written round `epoch`; bounded wait.
 // Returns false (and records kStatusSync) if the group did not arrive.
 __device__ __forceinline__ bool group_arrive_wait(unsigned* ctr, unsigned target, int spin_limit, WsHeader* hdr,
@@ -194,7 +208,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   __shared__ int s_flag;
 
   const int s = p.group_size;
-  const int q = member_spread(blockIdx.x);
+  const int q = p.xcd_members > 0 ? xcd_tiled(blockIdx.x, gridDim.x, s, p.xcd_members) : member_spread(blockIdx.x);
   const int g = q / s, j = q % s;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   __shared__ int s_flag;
 
   const int s = p.group_size;
-  const int q = xcd_major(blockIdx.x, gridDim.x);
+  const int q = p.xcd_members > 0 ? xcd_tiled(blockIdx.x, gridDim.x, s, p.xcd_members) : xcd_major(blockIdx.x, gridDim.x);
   const int g = q / s, j = q % s;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -488,7 +502,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
   __shared__ int s_flag;
 
   const int s = p.group_size;
-  const int q = member_spread(blockIdx.x);
+  const int q = p.xcd_members > 0 ? xcd_tiled(blockIdx.x, gridDim.x, s, p.xcd_members) : member_spread(blockIdx.x);
   const int g = q / s, j = q % s;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();

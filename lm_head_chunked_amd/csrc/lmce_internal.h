@@ -57,6 +57,7 @@ struct BwdArgs {
   int64_t L, H, V, ignore_index, Lpad, Vpad;
   int group_size;       // workgroups per group = H / HS (HS = 256 if H % 256 == 0, else 128)
   int n_groups;
+  int xcd_members;      // > 0: members of one group per XCD (xcd_tiled order); 0: the pass's default order
   int spin_limit;       // bound of every group wait
   unsigned* sync;       // [n_groups * kSyncStride] arrival counters, zeroed before the launch
   uint16_t* xbuf;       // [n_groups][2][2 * group_size][256][128] exchange slots
