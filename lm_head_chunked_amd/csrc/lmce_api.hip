@@ -170,21 +170,31 @@ extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int
 
 namespace {
 
-// Members of one dW group per XCD.  In a round, the workgroups of one XCD
-// that host `a` members of each of b = nwg / 8 / a groups read a distinct h
-// blocks and h^T slices and b distinct W tiles and exchange slots, each
-// through one L2, so the XCD fetches about 4 (a + b) tile-sized operands per
-// round: the valid a with the smallest a + b is taken (on the 8B head shape,
-// a = 8 cut the pass from 313 to 293 ms against a = 16, the whole group on
-// one XCD).  0 (whole groups per XCD, xcd_major) when no a is valid.
-int dw_xcd_members(int s, int nwg) {
+// Members of one group per XCD (xcd_tiled order), or 0 for the pass's
+// default order.  In a round, every member reads two operands of its own
+// (the producer's 256 x H tile and the consumer's H slice over the round's
+// 256 s blocks: 512 H bytes each, shared with the same member of the other
+// groups) and two of its group (the producer's other 256 x H tile and the
+// exchange slot of s 256 x 256 bf16 tiles).  The workgroups of one XCD that
+// host a members of each of b = nwg / 8 / a groups read about
+// 1024 H a + (512 H + 131072 s) b bytes per round through their L2, that is
+// 2a + 2b tile-sized units for 256-wide slices and 2a + 3b for 128-wide ones;
+// the valid a with the smallest cost is taken.  Ties are broken as measured
+// on the 8B head shard (same-box A/B, 256-wide slices, a = 4 or 8): the dW
+// pass takes the larger a (a = 8 against whole groups per XCD cut it from
+// 305.6 to 296.9 ms), the passes whose groups own row blocks the smaller one
+// (the training forward ran 299.9 ms with a = 4 against 308.7 with a = 8).
+int group_xcd_members(int pass, int hs, int s, int nwg) {
   if (nwg % 8 != 0) return 0;
+  const int c = hs == 256 ? 2 : 3;
+  const bool larger = pass == kPassDw;
   int best = 0, cost = 1 << 30;
-  for (int a = s; a >= 1; --a) {
+  for (int i = 1; i <= s; ++i) {
+    const int a = larger ? s + 1 - i : i;
     if (s % a != 0 || 8 % (s / a) != 0 || (nwg / 8) % a != 0) continue;
-    const int c = a + (nwg / 8) / a;
-    if (c < cost) {
-      cost = c;
+    const int k = 2 * a + c * ((nwg / 8) / a);
+    if (k < cost) {
+      cost = k;
       best = a;
     }
   }
@@ -195,10 +205,7 @@ int dw_xcd_members(int s, int nwg) {
 // blocks): picks the H slice width, sizes the cooperative grid to the
 // resident workgroups, resets the group counters and launches.
 int launch_group_pass(int pass, BwdArgs& a, const Plan& p, int64_t items, hipStream_t s) {
-  // The fused training forward always takes 128-wide slices: its 256-wide
-  // form (accumulator parked between rounds) gave results that differed
-  // from run to run, and stays disabled until that is understood.
-  int hs = pass == kPassFwdDh ? 128 : p.hs;
+  int hs = p.hs;
   int resident = 0;
   if (bwd_resident_wgs(pass, hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
   if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
@@ -216,7 +223,7 @@ int launch_group_pass(int pass, BwdArgs& a, const Plan& p, int64_t items, hipStr
   if (groups < 1) return LMCE_ERR_UNSUPPORTED;
   a.group_size = group_size;
   a.n_groups = (int)groups;
-  a.xcd_members = pass == kPassDw ? dw_xcd_members(group_size, (int)groups * group_size) : 0;
+  a.xcd_members = group_xcd_members(pass, hs, group_size, (int)groups * group_size);
   if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
   if (launch_bwd_group(pass, a, hs, (int)groups * group_size, s) != hipSuccess) return LMCE_ERR_HIP;
   return LMCE_OK;

@@ -58,8 +58,8 @@ __global__ void k_zero_u32(unsigned* __restrict__ p, int n) {
 }
 
 // Position of workgroup b in XCD-major order (workgroups are dispatched to
-// the 8 XCDs round-robin), so that the members of a group share an L2.  Used
-// by the dW pass, whose members all load their group's vocabulary tile of W.
+// the 8 XCDs round-robin), so that the members of a group share an L2: the
+// dW pass's order when xcd_tiled does not apply.
 __device__ __forceinline__ int xcd_major(int b, int nwg) {
   if (nwg % 8 != 0) return b;
   return (b & 7) * (nwg >> 3) + (b >> 3);
@@ -67,12 +67,12 @@ __device__ __forceinline__ int xcd_major(int b, int nwg) {
 
 // Position of workgroup b with the members of each group spread over the
 // XCDs: b = g * s + j, so member j of every group sits on XCD (g * s + j) % 8,
-// which is j % 8 for all groups when s is a multiple of 8.  Used by the
-// passes whose groups own row blocks: in a round, member j of every group
-// loads the same vocabulary tile of W (and the same H slice of W^T), so
-// groups that share an XCD read it through one L2 instead of each fetching
-// it from HBM or the Infinity Cache.  The exchange then crosses XCDs, which
-// its device-coherent stores and loads allow.
+// which is j % 8 for all groups when s is a multiple of 8.  The order of the
+// passes whose groups own row blocks when xcd_tiled does not apply: in a
+// round, member j of every group loads the same vocabulary tile of W (and the
+// same H slice of W^T), so groups that share an XCD read it through one L2.
+// The exchange then crosses XCDs, which its device-coherent stores and loads
+// allow.
 __device__ __forceinline__ int member_spread(int b) { return b; }
 
 // Position of workgroup b when every XCD hosts `a` members of each of
@@ -187,7 +187,7 @@ __device__ __forceinline__ void gstage_flush(const char* lds, rsrc_t rslot, int 
     const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
         (const __attribute__((address_space(3))) char*)lds + row * 512 + ((c ^ (row & 31)) << 4));
     const uint32_t voff = (uint32_t)(((c >> 4) * 256 * 128 + row * 128 + (c & 15) * 8) * 2);
-    store_sc1_b128(rslot, voff, (uint32_t)j * 2u * 256u * 128u * 2u, v);
+    store_sc1_b128(rslot, voff + (uint32_t)j * 2u * 256u * 128u * 2u, v);
   }
 }
 
@@ -471,7 +471,7 @@ __device__ __forceinline__ void gstage_flush_scaled(const char* lds, const float
     const u32x4 w = {__builtin_bit_cast(u32x2, blo)[0], __builtin_bit_cast(u32x2, blo)[1],
                      __builtin_bit_cast(u32x2, bhi)[0], __builtin_bit_cast(u32x2, bhi)[1]};
     const uint32_t voff = (uint32_t)(((c >> 4) * 256 * 128 + row * 128 + (c & 15) * 8) * 2);
-    store_sc1_b128(rslot, voff, (uint32_t)j * 2u * 256u * 128u * 2u, w);
+    store_sc1_b128(rslot, voff + (uint32_t)j * 2u * 256u * 128u * 2u, w);
   }
 }
 
@@ -706,8 +706,9 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
 }
 
 const void* bwd_kernel(int pass, int hs) {
-  if (hs == 256 && pass != kPassFwdDh) {
+  if (hs == 256) {
     if (pass == kPassDh) return reinterpret_cast<const void*>(&k_bwd_dh<256>);
+    if (pass == kPassFwdDh) return reinterpret_cast<const void*>(&k_fwd_dh<256>);
     return reinterpret_cast<const void*>(&k_bwd_dW<256>);
   }
   if (pass == kPassDh) return reinterpret_cast<const void*>(&k_bwd_dh<128>);

@@ -335,9 +335,16 @@ __device__ __forceinline__ void store_sc1_b64(rsrc_t rs, uint32_t voff, uint32_t
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, voff, soff, kAuxSc1);
 }
 
-// 16-byte buffer store, coherent at device scope.
-__device__ __forceinline__ void store_sc1_b128(rsrc_t rs, uint32_t voff, uint32_t soff, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, soff, kAuxSc1);
+// 16-byte buffer store, coherent at device scope.  The whole offset goes in
+// the vector offset and the scalar offset is the constant 0: for a buffer
+// store of more than 8 bytes whose scalar offset is an SGPR, the compiler
+// puts no wait state between the store and a VALU write of its data
+// registers, and on gfx950 such a write can reach the data before the store
+// has read it (a training-forward build that reused the registers at once
+// wrote wrong exchange tiles from run to run).  With a constant scalar
+// offset the compiler separates the two itself.
+__device__ __forceinline__ void store_sc1_b128(rsrc_t rs, uint32_t voff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, 0, kAuxSc1);
 }
 
 // 4-byte buffer store and load, coherent at device scope.
