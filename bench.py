@@ -73,8 +73,14 @@ def recorded_traffic(workload, kernel):
     return int(m.group(1)) if m else None
 
 
-def cpu_baseline(wl, W_cpu, h_rows, y_rows):
-    """fp64 oracle on the first rows of the workload at full H and V."""
+def cpu_baseline(wl, W_cpu, h_rows, y_rows, n_valid):
+    """fp64 oracle on the first rows of the workload at full H and V.
+
+    Returns the timing record and the oracle's result for those rows.  Every
+    row's lse depends on that row alone and its dh on the row and the
+    workload's count N of rows with a label, so the upstream gradient
+    n_sub / N (n_sub: labelled rows of the sample) makes the oracle's dh rows
+    those of the whole workload."""
     import numpy as np
     import threadpoolctl
 
@@ -84,15 +90,18 @@ def cpu_baseline(wl, W_cpu, h_rows, y_rows):
     y_np = y_rows.numpy()
     W_np = W_cpu.float().numpy()
     oracle.forward(h_np[:8], W_np, y_np[:8])  # warm BLAS
+    n_sub = int((y_np != -100).sum())
+    grad = n_sub / n_valid if n_sub > 0 and n_valid > 0 else 1.0
     t0 = time.perf_counter()
-    oracle.fwd_bwd(h_np, W_np, y_np)
+    ref = oracle.fwd_bwd(h_np, W_np, y_np, grad=grad)
     dt = time.perf_counter() - t0
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [os.cpu_count()])
     n = h_np.shape[0]
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    info = {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {n} rows of {wl.name} at full H={wl.H}, V={wl.V}: fp64 forward+backward in "
                       f"{dt:.2f} s (full workload extrapolates to {wl.L / n * dt:.0f} s)"}
+    return info, ref
 
 
 def main():
@@ -238,13 +247,27 @@ def main():
             "traffic": recorded_traffic(wl.name, dom_kernel), "mean_ms": call_ms[dom],
         },
         "cpu_baseline": None,
+        "parity": None,
     }
+    n_rows = min(args.cpu_rows, L)
+    lse_rows = lse[:n_rows].cpu().numpy()
+    dh_rows = dh[:n_rows].cpu().numpy()
     del dh, dW, ws
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        import numpy as np
+
+        log(f"[bench] cpu baseline: oracle on {n_rows} rows")
         W_cpu = W.cpu()
-        result["cpu_baseline"] = cpu_baseline(wl, W_cpu, h[: args.cpu_rows].cpu(), y[: args.cpu_rows].cpu())
+        result["cpu_baseline"], ref = cpu_baseline(wl, W_cpu, h[:n_rows].cpu(), y[:n_rows].cpu(), n_valid)
         log(f"[bench] cpu baseline {result['cpu_baseline']['value']:.1f} tokens/s")
+        # the last timed step's lse and dh on the sampled rows against the oracle
+        e_lse = float(np.max(np.abs(lse_rows - ref["lse"])))
+        nref = float(np.linalg.norm(ref["dh"]))
+        e_dh = float(np.linalg.norm(dh_rows - ref["dh"]) / nref) if nref > 0 else float(np.linalg.norm(dh_rows))
+        result["parity"] = {"rows": n_rows, "reference": "fp64 oracle on the same rows (dh for the workload's N)",
+                            "lse_max_abs_err": e_lse, "lse_tol": 2e-3, "dh_rel_fro_err": e_dh, "dh_tol": 1e-2,
+                            "within_tol": bool(e_lse <= 2e-3 and e_dh <= 1e-2)}
+        log(f"[bench] parity on {n_rows} rows: lse max abs err {e_lse:.2e}, dh rel err {e_dh:.2e}")
     print(json.dumps(result), flush=True)
 
 
