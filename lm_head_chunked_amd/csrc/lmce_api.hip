@@ -172,15 +172,16 @@ namespace {
 
 // Members of one group per XCD (xcd_tiled order), or 0 for the pass's
 // default order.  In a round, every member reads two operands of its own
-// (the producer's 256 x H tile and the consumer's H slice over the round's
-// 256 s blocks: 512 H bytes each, shared with the same member of the other
-// groups) and two of its group (the producer's other 256 x H tile and the
+// (the producer's 256 x H tile, and the consumer's HS columns of W^T or h^T
+// over the round's 256 s vocabulary or token rows: 512 H bytes each, shared
+// with the same member of the other groups) and two of its group (the producer's other 256 x H tile and the
 // exchange slot of s 256 x 256 bf16 tiles).  The workgroups of one XCD that
 // host a members of each of b = nwg / 8 / a groups read about
 // 1024 H a + (512 H + 131072 s) b bytes per round through their L2, that is
 // 2a + 2b tile-sized units for 256-wide slices and 2a + 3b for 128-wide ones;
 // the valid a with the smallest cost is taken.  Ties are broken as measured
-// on the 8B head shard (same-box A/B, 256-wide slices, a = 4 or 8): the dW
+// on the Qwen3-8B head shape with 131072 rows (H = 4096, V = 151936; A/B runs
+// of both builds on one GPU, 256-wide slices, a = 4 or 8): the dW
 // pass takes the larger a (a = 8 against whole groups per XCD cut it from
 // 305.6 to 296.9 ms), the passes whose groups own row blocks the smaller one
 // (the training forward ran 299.9 ms with a = 4 against 308.7 with a = 8).
