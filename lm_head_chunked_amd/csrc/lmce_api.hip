@@ -22,7 +22,8 @@ struct Plan {
   int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
   int64_t Lpad, Vpad;
   int hs, xbuf_wgs;
-  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, off_xstat, off_O, total;
+  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, off_xstat, off_O, off_cnt, off_crow,
+      off_clab, off_clse, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -89,6 +90,16 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   // training forward: O = sum_v softmax(z)_v W_v of every row, fp32 [L][H]
   p->off_O = off;
   off = align256(off + sizeof(float) * (size_t)L * (size_t)H);
+  // dW pass on the labelled rows only: per-chunk counts, then their index,
+  // label and lse (their h rows go to the W^T area, free during that pass)
+  p->off_cnt = off;
+  off = align256(off + sizeof(int) * (size_t)((L + 1023) / 1024));
+  p->off_crow = off;
+  off = align256(off + sizeof(int) * (size_t)L);
+  p->off_clab = off;
+  off = align256(off + sizeof(int64_t) * (size_t)L);
+  p->off_clse = off;
+  off = align256(off + sizeof(float) * (size_t)L);
   p->total = off;
   return LMCE_OK;
 }
@@ -254,7 +265,20 @@ BwdArgs group_args(const Plan& p, const void* h, const void* W, const int64_t* l
   a.part_m = at<float>(workspace, p.off_pm);
   a.part_s = at<float>(workspace, p.off_ps);
   a.hdr = at<WsHeader>(workspace, 0);
+  a.crow = at<int>(workspace, p.off_crow);
+  a.clab = at<int64_t>(workspace, p.off_clab);
+  a.clse = at<float>(workspace, p.off_clse);
+  a.ch = at<uint16_t>(workspace, p.off_WT);
   return a;
+}
+
+// Runs the dW pass: compacts the labelled rows (if that saves a 256-row
+// block), builds h^T of the rows swept, then the group pass.  Overwrites the
+// W^T area, so it comes after every pass that reads W^T.
+int dw_pass(BwdArgs& a, const Plan& p, void* workspace, hipStream_t s) {
+  if (launch_compact(a, at<int>(workspace, p.off_cnt), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (launch_transpose_dw_rows(a, at<uint16_t>(workspace, p.off_hT), s) != hipSuccess) return LMCE_ERR_HIP;
+  return launch_group_pass(kPassDw, a, p, (p.V + 255) / 256, s);
 }
 
 // Shared by lmce_bwd, lmce_bwd_dh and lmce_bwd_dW: which = 1 (dh), 2 (dW), 3 (both).
@@ -277,14 +301,13 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
   a.grad_loss = grad_loss;
   a.dh = dh_out;
   a.dW = dW_out;
-  if ((which & 2) && launch_transpose(h, L, H, at<uint16_t>(workspace, p.off_hT), p.Lpad, s) != hipSuccess) return LMCE_ERR_HIP;
-  if ((which & 1) && launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
   if (which & 1) {
+    if (launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
     st = launch_group_pass(kPassDh, a, p, (L + 255) / 256, s);
     if (st != LMCE_OK) return st;
   }
   if (which & 2) {
-    st = launch_group_pass(kPassDw, a, p, (V + 255) / 256, s);
+    st = dw_pass(a, p, workspace, s);
     if (st != LMCE_OK) return st;
   }
   return LMCE_OK;
@@ -368,8 +391,7 @@ extern "C" int lmce_bwd_train(const void* h, const void* W, const int64_t* label
   a.dh = dh_out;
   a.dW = dW_out;
   if (launch_dh_finish(a, s) != hipSuccess) return LMCE_ERR_HIP;
-  if (launch_transpose(h, L, H, at<uint16_t>(workspace, p.off_hT), p.Lpad, s) != hipSuccess) return LMCE_ERR_HIP;
-  return launch_group_pass(kPassDw, a, p, (V + 255) / 256, s);
+  return dw_pass(a, p, workspace, s);
 }
 
 extern "C" int lmce_read_status(const void* workspace, void* stream) {

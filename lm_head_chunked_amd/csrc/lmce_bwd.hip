@@ -52,6 +52,120 @@ __global__ __launch_bounds__(256) void k_transpose(const u16* __restrict__ in, i
   }
 }
 
+// ------------------------------------------------ labelled-row compaction
+// Rows without a label (ignore_index) carry no gradient: their G row is 0 and
+// they add nothing to dW.  When dropping them saves at least one 256-row
+// block, the dW pass sweeps only the labelled rows, in their original order
+// (a stable compaction, so the results are repeatable).
+
+// Labelled rows of each 1024-row chunk.
+__global__ __launch_bounds__(256) void k_count_chunks(const int64_t* __restrict__ labels, int64_t L, int64_t V,
+                                                      int64_t ignore_index, int* __restrict__ cnt) {
+  __shared__ int red[256];
+  const int64_t base = (int64_t)blockIdx.x * 1024;
+  int c = 0;
+  for (int i = threadIdx.x; i < 1024; i += 256) {
+    const int64_t r = base + i;
+    if (r < L) {
+      const int64_t y = labels[r];
+      c += (y != ignore_index && y >= 0 && y < V) ? 1 : 0;
+    }
+  }
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) cnt[blockIdx.x] = red[0];
+}
+
+// Decides the compaction (every block reaches the same decision from the
+// same counts) and writes, for the labelled rows of its chunk in order, their
+// index, label and lse.  ch_rows: rows the W^T area can hold.
+__global__ __launch_bounds__(1024) void k_compact_rows(const int64_t* __restrict__ labels, const float* __restrict__ lse,
+                                                       int64_t L, int64_t V, int64_t ignore_index, int64_t ch_rows,
+                                                       const int* __restrict__ cnt, int nchunks, WsHeader* hdr,
+                                                       int* __restrict__ crow, int64_t* __restrict__ clab,
+                                                       float* __restrict__ clse) {
+  __shared__ int scan[1024];
+  __shared__ int s_before, s_total;
+  if (threadIdx.x == 0) {
+    int before = 0, total = 0;
+    for (int b = 0; b < nchunks; ++b) {
+      if (b < (int)blockIdx.x) before += cnt[b];
+      total += cnt[b];
+    }
+    s_before = before;
+    s_total = total;
+  }
+  __syncthreads();
+  const int64_t n = s_total;
+  const bool compact = (n + 255) / 256 < (L + 255) / 256 && n <= ch_rows;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    hdr->compact = compact ? 1 : 0;
+    hdr->n_compact = compact ? (int)n : 0;
+  }
+  if (!compact) return;
+  const int64_t r = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  int64_t y = ignore_index;
+  if (r < L) y = labels[r];
+  const int f = (r < L && y != ignore_index && y >= 0 && y < V) ? 1 : 0;
+  scan[threadIdx.x] = f;
+  __syncthreads();
+  // inclusive scan over the block (Hillis-Steele)
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = (int)threadIdx.x >= d ? scan[threadIdx.x - d] : 0;
+    __syncthreads();
+    scan[threadIdx.x] += v;
+    __syncthreads();
+  }
+  if (f) {
+    const int64_t pos = s_before + scan[threadIdx.x] - 1;
+    crow[pos] = (int)r;
+    clab[pos] = y;
+    clse[pos] = lse[r];
+  }
+}
+
+// h rows of the labelled rows, in order, into the W^T area (one row per
+// block; rows past the compaction's own count exit).
+__global__ __launch_bounds__(256) void k_gather_rows(const u16* __restrict__ h, int64_t H, const WsHeader* hdr,
+                                                     const int* __restrict__ crow, u16* __restrict__ ch) {
+  if (hdr->compact == 0 || (int)blockIdx.x >= hdr->n_compact) return;
+  const int64_t src = crow[blockIdx.x];
+  const uint4* in = reinterpret_cast<const uint4*>(h + src * H);
+  uint4* out = reinterpret_cast<uint4*>(ch + (int64_t)blockIdx.x * H);
+  for (int64_t c = threadIdx.x; c < H / 8; c += 256) out[c] = in[c];
+}
+
+// h^T (tile-major, as k_transpose) of the rows the dW pass sweeps: the
+// compacted rows when hdr->compact, else all L rows of h.  The grid covers
+// ceil(L / 64) row tiles; tiles past the swept rows' 128-row padding exit.
+__global__ __launch_bounds__(256) void k_transpose_dw_rows(const u16* __restrict__ h, const u16* __restrict__ ch,
+                                                           int64_t L, int64_t C, const WsHeader* hdr,
+                                                           u16* __restrict__ out) {
+  __shared__ u16 t[64][66];
+  const bool compact = hdr->compact != 0;
+  const u16* in = compact ? ch : h;
+  const int64_t R = compact ? (int64_t)hdr->n_compact : L;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  if (r0 >= (R + 127) / 128 * 128) return;
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i >> 6, cc = i & 63;
+    const int64_t r = r0 + rr;
+    t[rr][cc] = (r < R) ? in[r * C + c0 + cc] : (u16)0;
+  }
+  __syncthreads();
+  const int64_t tile = r0 >> 7;
+  const int64_t rin = r0 & 127;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i >> 6, rr = i & 63;
+    out[(tile * C + c0 + cc) * 128 + rin + rr] = t[rr][cc];
+  }
+}
+
 __global__ void k_zero_u32(unsigned* __restrict__ p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -329,10 +443,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t H = p.H, V = p.V, L = p.L;
+  const int64_t H = p.H, V = p.V, L_all = p.L;
   const int64_t c0 = (int64_t)j * HS;
   const rsrc_t park = make_rsrc(p.park + (int64_t)blockIdx.x * (kParkPerWG / 4), kPark ? kParkPerWG : 0);  // this workgroup's parking area
   const int64_t slot_elems = (int64_t)s * 256 * 256;
+  // the rows swept: the compacted labelled rows when hdr->compact, else all
+  const bool compact = p.hdr->compact != 0;
+  const int64_t L = compact ? (int64_t)p.hdr->n_compact : L_all;
+  const u16* const hrows = compact ? p.ch : p.h;
+  const int64_t* const labels = compact ? p.clab : p.labels;
+  const float* const lse = compact ? p.clse : p.lse;
   const int rt256 = (int)((L + 255) / 256);
   const int rt128 = (int)((L + 127) / 128);
   const int rounds = (rt256 + s - 1) / s;
@@ -355,16 +475,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
         const int64_t rend = min(r0 + 256, L);
         if (threadIdx.x < 256) {
           const int64_t t = r0 + threadIdx.x;
-          const int64_t y = t < rend ? p.labels[t] : p.ignore_index;
+          const int64_t y = t < rend ? labels[t] : p.ignore_index;
           const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
           row_lab[threadIdx.x] = (valid && y >= v0 && y < v0 + 256) ? (int)(y - v0) : -1;
           row_scale[threadIdx.x] = valid ? gscale : 0.f;
-          row_lse2[threadIdx.x] = t < rend ? p.lse[t] * kLog2e : INFINITY;
+          row_lse2[threadIdx.x] = t < rend ? lse[t] * kLog2e : INFINITY;
         }
         f32x16 z[P::MB][P::NB];
         zero_acc(z);
         // (the GEMM's first barrier orders the row_* writes before their use)
-        P::run(linear_operand(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2)), ow, (int)H, lds, z);
+        P::run(linear_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2)), ow, (int)H, lds, z);
         // G^T[v][token]: lane = v (column), 4 consecutive tokens per store.
         // Token data is read once per 4-token group and reused for the
         // lane's 4 vocabulary columns; columns past V get a zero factor.
@@ -697,6 +817,27 @@ __global__ __launch_bounds__(256) void k_dh_finish(BwdArgs p) {
 hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st) {
   dim3 grid((unsigned)(Rpad / 64), (unsigned)(C / 64));
   hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, st, (const u16*)in, R, C, (u16*)out, Rpad);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream_t st) {
+  const int nchunks = (int)((a.L + 1023) / 1024);
+  hipLaunchKernelGGL(k_count_chunks, dim3((unsigned)nchunks), dim3(256), 0, st, a.labels, a.L, a.V, a.ignore_index, cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_compact_rows, dim3((unsigned)nchunks), dim3(1024), 0, st, a.labels, a.lse, a.L, a.V,
+                     a.ignore_index, ch_rows, (const int*)cnt, nchunks, a.hdr, a.crow, a.clab, a.clse);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)a.L), dim3(256), 0, st, a.h, a.H, (const WsHeader*)a.hdr,
+                     (const int*)a.crow, a.ch);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_dw_rows(const BwdArgs& a, void* hT, hipStream_t st) {
+  dim3 grid((unsigned)((a.L + 63) / 64), (unsigned)(a.H / 64));
+  hipLaunchKernelGGL(k_transpose_dw_rows, grid, dim3(256), 0, st, a.h, (const u16*)a.ch, a.L, a.H,
+                     (const WsHeader*)a.hdr, (u16*)hT);
   return hipGetLastError();
 }
 

@@ -24,7 +24,9 @@ struct WsHeader {
   int n_valid;   // rows whose label is not ignore_index (and is in range)
   int status;    // 0, or kStatusLabel | kStatusSync | kStatusState
   int saved;     // kSavedTag once a training forward has filled O, else 0
-  int pad[61];
+  int compact;   // 1 while the dW pass runs on the compacted labelled rows (set by k_compact_rows)
+  int n_compact; // rows written by that compaction (its own count of labelled rows)
+  int pad[59];
 };
 
 struct FwdArgs {
@@ -67,6 +69,13 @@ struct BwdArgs {
   float* part_m;        // [L] row max, fused forward output
   float* part_s;        // [L] row sum of exp(z - max), fused forward output
   WsHeader* hdr;
+  // The labelled rows in order (written by k_compact_rows when hdr->compact):
+  // their index, label and lse, and their h rows in the W^T area (free
+  // during the dW pass); the dW pass then sweeps hdr->n_valid rows.
+  int* crow;
+  int64_t* clab;
+  float* clse;
+  uint16_t* ch;
   float* dh;
   float* dW;
 };
@@ -76,6 +85,10 @@ hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int6
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
 hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
 hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st);
+// Compaction of the labelled rows for the dW pass (cnt: ceil(L / 1024) ints),
+// then h^T of the rows the dW pass sweeps (compacted or all L).
+hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream_t st);
+hipError_t launch_transpose_dw_rows(const BwdArgs& a, void* hT, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
 // Group-scheduled kernels: the two backward passes and the fused training forward.
 constexpr int kPassDh = 0, kPassDw = 1, kPassFwdDh = 2;
