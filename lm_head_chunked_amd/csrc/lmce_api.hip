@@ -23,7 +23,7 @@ struct Plan {
   int64_t Lpad, Vpad;
   int hs, xbuf_wgs;
   size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, off_xstat, off_O, off_cnt, off_crow,
-      off_clab, off_clse, total;
+      off_clab, off_clse, off_part, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -100,6 +100,10 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   off = align256(off + sizeof(int64_t) * (size_t)L);
   p->off_clse = off;
   off = align256(off + sizeof(float) * (size_t)L);
+  // dW pass: partial slices of its leftover vocabulary blocks (one 256 x HS
+  // fp32 slice per workgroup at most)
+  p->off_part = off;
+  off = align256(off + (size_t)wgs * kParkPerWG);
   p->total = off;
   return LMCE_OK;
 }
@@ -238,6 +242,7 @@ int launch_group_pass(int pass, BwdArgs& a, const Plan& p, int64_t items, hipStr
   a.xcd_members = group_xcd_members(pass, hs, group_size, (int)groups * group_size);
   if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
   if (launch_bwd_group(pass, a, hs, (int)groups * group_size, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (pass == kPassDw && launch_dw_tail(a, hs, s) != hipSuccess) return LMCE_ERR_HIP;
   return LMCE_OK;
 }
 
@@ -269,6 +274,7 @@ BwdArgs group_args(const Plan& p, const void* h, const void* W, const int64_t* l
   a.clab = at<int64_t>(workspace, p.off_clab);
   a.clse = at<float>(workspace, p.off_clse);
   a.ch = at<uint16_t>(workspace, p.off_WT);
+  a.dw_part = at<float>(workspace, p.off_part);
   return a;
 }
 

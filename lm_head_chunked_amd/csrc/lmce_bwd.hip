@@ -166,6 +166,28 @@ __global__ __launch_bounds__(256) void k_transpose_dw_rows(const u16* __restrict
   }
 }
 
+// dW rows of the leftover blocks of the dW pass: block t of them was swept by
+// groups t * gpb .. t * gpb + gpb - 1, member j's partial 256 x HS slice of
+// group q at dw_part + (q * s + j) * 256 * HS; they are added in group order.
+// One workgroup per (block, member).
+__global__ __launch_bounds__(256) void k_dw_tail(const float* __restrict__ part, float* __restrict__ dW, int64_t V,
+                                                 int64_t H, int hs, int s, int gpb, int64_t v_first) {
+  const int t = blockIdx.x / s, j = blockIdx.x % s;
+  const int64_t v0 = v_first + (int64_t)t * 256;
+  for (int e = threadIdx.x * 4; e < 256 * hs; e += 1024) {
+    const int r = e / hs, c = e % hs;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < gpb; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)(t * gpb + q) * s + j) * 256 * hs + e);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    if (v0 + r < V) *reinterpret_cast<float4*>(dW + (v0 + r) * H + (int64_t)j * hs + c) = acc;
+  }
+}
+
 __global__ void k_zero_u32(unsigned* __restrict__ p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -461,12 +483,27 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
   unsigned epoch = 0;
 
-  for (int vb = g; vb < nvb; vb += p.n_groups) {
+  // Blocks g, g + n_groups, ... in lockstep with the other groups (member j of
+  // every group reads the same token block in the same round).  The blocks
+  // left over after the last whole wave are shared by all groups instead of
+  // keeping a few busy while the rest idle: n_groups / tail_blocks groups
+  // sweep consecutive round ranges of each, write partial slices, and
+  // k_dw_tail adds them up in a fixed order.
+  const int full_waves = nvb / p.n_groups;
+  const int tail_blocks = nvb - full_waves * p.n_groups;
+  const int gpb = tail_blocks > 0 ? p.n_groups / tail_blocks : 1;  // groups per leftover block
+  const int nwork = full_waves + ((tail_blocks > 0 && g < gpb * tail_blocks) ? 1 : 0);
+  for (int w = 0; w < nwork; ++w) {
+    const bool tail = w == full_waves;
+    const int vb = tail ? full_waves * p.n_groups + g / gpb : g + w * p.n_groups;
+    const int k_begin = tail ? (g % gpb) * rounds / gpb : 0;
+    const int k_end = tail ? (g % gpb + 1) * rounds / gpb : rounds;
+    const bool to_part = tail && gpb > 1;  // a partial slice, summed by k_dw_tail
     const int64_t v0 = (int64_t)vb * 256;
     const Operand ow = linear_operand(p.W + v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
     f32x16 dacc[C::MB][C::NB];
     if constexpr (!kPark) zero_acc(dacc);
-    for (int k = 0; k < rounds; ++k, ++epoch) {
+    for (int k = k_begin; k < k_end; ++k, ++epoch) {
       u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
       const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
       const int rt = k * s + j;
@@ -524,7 +561,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
         gstage_flush(lds, rslot, j);
       }
       if constexpr (kPark) {
-        if (k == 0) zero_acc(dacc);
+        if (k == k_begin) zero_acc(dacc);
         else unpark_acc(dacc, park, wave, lane);
       }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
@@ -536,13 +573,21 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
              lds, dacc);
       if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
     }
+    // (an empty round range, e.g. no labelled rows at all, leaves 0)
+    f32x16 fin[C::MB][C::NB];
     if constexpr (kPark) {
-      f32x16 fin[C::MB][C::NB];
-      unpark_acc(fin, park, wave, lane);
-      store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
+      if (k_end > k_begin) unpark_acc(fin, park, wave, lane);
+      else zero_acc(fin);
     } else {
-      store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) fin[mb][nb] = dacc[mb][nb];
     }
+    if (to_part)
+      store_tile_f32(p.dw_part + ((int64_t)g * s + j) * 256 * HS, 256, HS, HS, fin, wm * 64, wn * (HS / 2), lane);
+    else
+      store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
   }
 }
 
@@ -838,6 +883,18 @@ hipError_t launch_transpose_dw_rows(const BwdArgs& a, void* hT, hipStream_t st) 
   dim3 grid((unsigned)((a.L + 63) / 64), (unsigned)(a.H / 64));
   hipLaunchKernelGGL(k_transpose_dw_rows, grid, dim3(256), 0, st, a.h, (const u16*)a.ch, a.L, a.H,
                      (const WsHeader*)a.hdr, (u16*)hT);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_tail(const BwdArgs& a, int hs, hipStream_t st) {
+  const int nvb = (int)((a.V + 255) / 256);
+  const int full_waves = nvb / a.n_groups;
+  const int tail_blocks = nvb - full_waves * a.n_groups;
+  if (tail_blocks == 0) return hipSuccess;
+  const int gpb = a.n_groups / tail_blocks;
+  if (gpb < 2) return hipSuccess;  // each leftover block went whole to one group
+  hipLaunchKernelGGL(k_dw_tail, dim3((unsigned)(tail_blocks * a.group_size)), dim3(256), 0, st, (const float*)a.dw_part,
+                     a.dW, a.V, a.H, hs, a.group_size, gpb, (int64_t)full_waves * a.n_groups * 256);
   return hipGetLastError();
 }
 

@@ -76,6 +76,7 @@ struct BwdArgs {
   int64_t* clab;
   float* clse;
   uint16_t* ch;
+  float* dw_part;       // [group][member][256][HS] partial dW slices of the dW pass's leftover blocks
   float* dh;
   float* dW;
 };
@@ -95,5 +96,7 @@ constexpr int kPassDh = 0, kPassDw = 1, kPassFwdDh = 2;
 hipError_t bwd_resident_wgs(int pass, int hs, int* wgs);
 hipError_t launch_bwd_group(int pass, const BwdArgs& a, int hs, int n_wgs, hipStream_t st);
 hipError_t launch_dh_finish(const BwdArgs& a, hipStream_t st);
+// Sums the dW pass's partial slices of its leftover blocks (no-op when none).
+hipError_t launch_dw_tail(const BwdArgs& a, int hs, hipStream_t st);
 
 }  // namespace lmce

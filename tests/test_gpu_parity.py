@@ -329,6 +329,19 @@ def test_all_rows_ignored():
     assert np.all(gpu["dh"] == 0.0) and np.all(gpu["dW"] == 0.0)
 
 
+@pytest.mark.parametrize("train", [False, True], ids=["plain", "train"])
+def test_all_rows_ignored_wide_slices(train):
+    """No labelled row at H = 3072: the dW pass (256-wide slices, accumulators
+    parked between rounds) has no rows to sweep and must still write dW = 0."""
+    say(f"[case] N_valid = 0, H = 3072, train={train}")
+    h, W, y = synth.random_case(700, 3072, 3000, seed=9)
+    y[:] = -100
+    gpu = run_gpu(h, W, y, train=train)
+    assert math.isnan(gpu["loss"])
+    assert np.all(np.isfinite(gpu["lse"]))
+    assert np.all(gpu["dh"] == 0.0) and np.all(gpu["dW"] == 0.0)
+
+
 def test_out_of_range_label_is_reported():
     say("[case] bad label")
     h, W, y = synth.random_case(64, 128, 100, seed=6, ignore_frac=0.0)
