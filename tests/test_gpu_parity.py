@@ -295,6 +295,17 @@ def test_results_do_not_depend_on_chunk_rows():
         assert np.array_equal(o["dW"], base["dW"]), c
 
 
+def test_train_pair_does_not_depend_on_chunk_rows():
+    say("[case] chunk_rows independence, training pair, L=700 H=3072 V=3000")
+    h, W, y = synth.random_case(700, 3072, 3000, seed=6, ignore_frac=0.1)
+    base = run_gpu(h, W, y, chunk_rows=256, train=True)
+    for c in (32, 128, 1024):
+        o = run_gpu(h, W, y, chunk_rows=c, train=True)
+        assert o["loss"] == base["loss"], c
+        for k in ("lse", "dh", "dW"):
+            assert np.array_equal(o[k], base[k]), (c, k)
+
+
 def test_deterministic():
     say("[case] determinism tiny")
     h, W, y = synth.make("tiny")
