@@ -5,24 +5,30 @@
 // G = g/N * valid * (softmax - onehot), dh = G W and dW = G^T h.
 //
 // dh and dW are H wide: a 256 x H fp32 accumulator (4 MiB at H = 4096) does
-// not fit in one compute unit, so each pass runs as groups of s = H / 128
-// workgroups, workgroup j of a group owning a 128-wide slice of the
-// accumulator in registers.  In every round each member recomputes ONE
-// full-H 256 x 256 logit tile with MFMA, turns it into bf16 G in registers
-// and writes it to the group's exchange slot; after a group barrier every
-// member contracts all s tiles of the round into its own slice.  Each logit
-// is thus recomputed exactly once per pass and no logit or G tile exists for
-// more than one round (the exchange holds 2 x s tiles per group).
+// not fit in one compute unit, so each pass runs as groups of s = H / HS
+// workgroups, workgroup j of a group owning an HS-wide slice of the
+// accumulator (HS = 128 in registers, or 256 parked in the workspace between
+// rounds).  In every round each member recomputes ONE full-H 256 x 256 logit
+// tile with MFMA, turns it into bf16 G in registers and writes it to the
+// group's exchange slot; after a group barrier every member contracts all s
+// tiles of the round into its own slice.  Each logit is thus recomputed
+// exactly once per pass and no logit or G tile exists for more than one
+// round (the exchange holds 2 x s tiles per group).
 //
 //   k_bwd_dh : group = 256 rows of h; rounds sweep the vocabulary, 256 per
 //              member; dh[rows][slice] += G W   (row-owned, no atomics)
 //   k_bwd_dW : group = 256 vocabulary rows; rounds sweep the tokens, 256 per
 //              member; dW[rows][slice] += G^T h (vocabulary-owned, no atomics)
+//              over the labelled rows only when that saves a block
+//              (k_compact_rows), the leftover vocabulary blocks split over
+//              all groups and summed by k_dw_tail
+//   k_fwd_dh : the training forward, the groups and rounds of k_bwd_dh with
+//              an online softmax: lse of every row and O = sum_v softmax W_v
 //
-// The groups run as one cooperative launch (all workgroups resident).  The
-// exchange uses device-coherent (sc1) stores and loads and a per-group
-// arrival counter; every wait is bounded and reports a sync error instead of
-// hanging.
+// The groups run as one cooperative launch (all workgroups resident), placed
+// on the XCDs as the host chooses (xcd_tiled).  The exchange uses
+// device-coherent (sc1) stores and loads and a per-group arrival counter;
+// every wait is bounded and reports a sync error instead of hanging.
 
 #include "lmce_device.h"
 #include "lmce_internal.h"
