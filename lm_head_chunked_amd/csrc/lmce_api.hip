@@ -23,7 +23,7 @@ struct Plan {
   int64_t Lpad, Vpad;
   int hs, xbuf_wgs;
   size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, off_xstat, off_O, off_cnt, off_crow,
-      off_clab, off_clse, off_part, total;
+      off_clab, off_clse, off_part, off_fperm, off_finv, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -104,6 +104,12 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   // fp32 slice per workgroup at most)
   p->off_part = off;
   off = align256(off + (size_t)wgs * kParkPerWG);
+  // training forward: labelled-first order of the rows and its inverse (the
+  // reordered h rows go to the h^T area, free during the forward)
+  p->off_fperm = off;
+  off = align256(off + sizeof(int) * (size_t)L);
+  p->off_finv = off;
+  off = align256(off + sizeof(int) * (size_t)L);
   p->total = off;
   return LMCE_OK;
 }
@@ -159,7 +165,8 @@ extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int
 
   WsHeader* hdr = at<WsHeader>(workspace, 0);
   if (launch_count_labels(labels, L, V, ignore_index, hdr, 0, s) != hipSuccess) return LMCE_ERR_HIP;
-  FwdArgs a;
+  FwdArgs a = {};
+  a.finv = nullptr;  // the plain forward keeps the rows in their order
   a.h = static_cast<const uint16_t*>(h);
   a.W = static_cast<const uint16_t*>(W);
   a.labels = labels;
@@ -189,8 +196,9 @@ namespace {
 // default order.  In a round, every member reads two operands of its own
 // (the producer's 256 x H tile, and the consumer's HS columns of W^T or h^T
 // over the round's 256 s vocabulary or token rows: 512 H bytes each, shared
-// with the same member of the other groups) and two of its group (the producer's other 256 x H tile and the
-// exchange slot of s 256 x 256 bf16 tiles).  The workgroups of one XCD that
+// with the same member of the other groups) and two of its group (the
+// producer's other 256 x H tile and the exchange slot of s 256 x 256 bf16
+// tiles).  The workgroups of one XCD that
 // host a members of each of b = nwg / 8 / a groups read about
 // 1024 H a + (512 H + 131072 s) b bytes per round through their L2, that is
 // 2a + 2b tile-sized units for 256-wide slices and 2a + 3b for 128-wide ones;
@@ -275,6 +283,9 @@ BwdArgs group_args(const Plan& p, const void* h, const void* W, const int64_t* l
   a.clse = at<float>(workspace, p.off_clse);
   a.ch = at<uint16_t>(workspace, p.off_WT);
   a.dw_part = at<float>(workspace, p.off_part);
+  a.fperm = at<int>(workspace, p.off_fperm);
+  a.finv = at<int>(workspace, p.off_finv);
+  a.hp = at<uint16_t>(workspace, p.off_hT);
   return a;
 }
 
@@ -357,6 +368,7 @@ extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* label
   WsHeader* hdr = at<WsHeader>(workspace, 0);
   if (launch_count_labels(labels, L, V, ignore_index, hdr, kSavedTag, s) != hipSuccess) return LMCE_ERR_HIP;
   BwdArgs a = group_args(p, h, W, labels, ignore_index, workspace);
+  if (launch_permute(a, at<int>(workspace, p.off_cnt), s) != hipSuccess) return LMCE_ERR_HIP;
   if (launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
   st = launch_group_pass(kPassFwdDh, a, p, (L + 255) / 256, s);
   if (st != LMCE_OK) return st;
@@ -375,6 +387,7 @@ extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* label
   f.part_m = a.part_m;
   f.part_s = a.part_s;
   f.block_sum = at<float>(workspace, p.off_bsum);
+  f.finv = a.finv;
   if (launch_fwd_rows(f, loss_out, lse_out, s) != hipSuccess) return LMCE_ERR_HIP;
   return LMCE_OK;
 }

@@ -134,6 +134,65 @@ __global__ __launch_bounds__(1024) void k_compact_rows(const int64_t* __restrict
   }
 }
 
+// Training forward: when it saves at least one 256-row block, a stable
+// labelled-first order of the rows (labelled rows at positions 0 .. n-1 in
+// their order, the others after them in theirs): fperm[position] = row,
+// finv[row] = position.  Row blocks made only of unlabelled rows then compute
+// lse alone, without the O contraction.
+__global__ __launch_bounds__(1024) void k_permute_rows(const int64_t* __restrict__ labels, int64_t L, int64_t V,
+                                                       int64_t ignore_index, const int* __restrict__ cnt, int nchunks,
+                                                       WsHeader* hdr, int* __restrict__ fperm, int* __restrict__ finv) {
+  __shared__ int scan[1024];
+  __shared__ int s_before, s_total;
+  if (threadIdx.x == 0) {
+    int before = 0, total = 0;
+    for (int b = 0; b < nchunks; ++b) {
+      if (b < (int)blockIdx.x) before += cnt[b];
+      total += cnt[b];
+    }
+    s_before = before;
+    s_total = total;
+  }
+  __syncthreads();
+  const int64_t n = s_total;
+  const bool compact = (n + 255) / 256 < (L + 255) / 256;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    hdr->fcompact = compact ? 1 : 0;
+    hdr->f_n = compact ? (int)n : 0;
+  }
+  if (!compact) return;
+  const int64_t r = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  int f = 0;
+  if (r < L) {
+    const int64_t y = labels[r];
+    f = (y != ignore_index && y >= 0 && y < V) ? 1 : 0;
+  }
+  scan[threadIdx.x] = f;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = (int)threadIdx.x >= d ? scan[threadIdx.x - d] : 0;
+    __syncthreads();
+    scan[threadIdx.x] += v;
+    __syncthreads();
+  }
+  if (r < L) {
+    const int64_t lab_before = s_before + scan[threadIdx.x] - f;  // labelled rows before r
+    const int64_t pos = f ? lab_before : n + (r - lab_before);
+    fperm[pos] = (int)r;
+    finv[r] = (int)pos;
+  }
+}
+
+// h rows in the labelled-first order (one row per block), when in use.
+__global__ __launch_bounds__(256) void k_gather_perm(const u16* __restrict__ h, int64_t H, const WsHeader* hdr,
+                                                     const int* __restrict__ fperm, u16* __restrict__ hp) {
+  if (hdr->fcompact == 0) return;
+  const int64_t src = fperm[blockIdx.x];
+  const uint4* in = reinterpret_cast<const uint4*>(h + src * H);
+  uint4* out = reinterpret_cast<uint4*>(hp + (int64_t)blockIdx.x * H);
+  for (int64_t c = threadIdx.x; c < H / 8; c += 256) out[c] = in[c];
+}
+
 // h rows of the labelled rows, in order, into the W^T area (one row per
 // block; rows past the compaction's own count exit).
 __global__ __launch_bounds__(256) void k_gather_rows(const u16* __restrict__ h, int64_t H, const WsHeader* hdr,
@@ -146,8 +205,9 @@ __global__ __launch_bounds__(256) void k_gather_rows(const u16* __restrict__ h, 
 }
 
 // h^T (tile-major, as k_transpose) of the rows the dW pass sweeps: the
-// compacted rows when hdr->compact, else all L rows of h.  The grid covers
-// ceil(L / 64) row tiles; tiles past the swept rows' 128-row padding exit.
+// compacted rows when hdr->compact, else all L rows of h, zero up to the
+// next multiple of 128 rows.  The grid covers Lpad / 64 row tiles; tiles past
+// the swept rows' 128-row padding exit.
 __global__ __launch_bounds__(256) void k_transpose_dw_rows(const u16* __restrict__ h, const u16* __restrict__ ch,
                                                            int64_t L, int64_t C, const WsHeader* hdr,
                                                            u16* __restrict__ out) {
@@ -689,12 +749,19 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
   const int vt128 = (int)((V + 127) / 128);
   const int rounds = (vt256 + s - 1) / s;
   const int nrb = (int)((L + 255) / 256);
+  // rows in the labelled-first order when the host-side plan found it worth
+  // a block (every output of this kernel is then indexed by position)
+  const bool reordered = p.hdr->fcompact != 0;
+  const int64_t n_lab = reordered ? (int64_t)p.hdr->f_n : L;
+  const u16* const hrows = reordered ? p.hp : p.h;
   unsigned epoch = 0, nbar = 0;
 
   for (int rb = g; rb < nrb; rb += p.n_groups) {
     const int64_t r0 = (int64_t)rb * 256;
     const int64_t rend = min(r0 + 256, L);
-    const Operand oh = linear_operand(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
+    // a block with no labelled row needs lse only: no P exchange, no O
+    const bool o_block = r0 < n_lab;
+    const Operand oh = linear_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
     if (t < 256) row_m[t] = -INFINITY;  // ordered by the barriers below
     float ssum[4] = {0.f, 0.f, 0.f, 0.f};  // lane's sums of exp(z - M) for its 4 tokens
     f32x16 dacc[C::MB][C::NB];
@@ -770,6 +837,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
         const int tok = wn * 128 + nb * 32 + (lane & 31);
         ssum[nb] = __builtin_fmaf(ssum[nb], row_a[tok], psum[nb] * row_f[tok]);
       }
+      if (!o_block) continue;  // (uniform over the group: every member takes the same block)
       if (produce) gstage_flush_scaled(lds, row_f, rslot, j);
       if constexpr (kPark) {
         if (k == 0) zero_acc(dacc);
@@ -814,6 +882,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
       }
     }
     __syncthreads();
+    if (!o_block) continue;
     f32x16 fin[C::MB][C::NB];
     if constexpr (kPark) unpark_acc(fin, park, wave, lane);
     else {
@@ -846,7 +915,8 @@ __global__ __launch_bounds__(256) void k_dh_finish(BwdArgs p) {
   const float scale = *p.grad_loss / (float)(n > 0 ? n : 1);
   if (!ok && r == 0 && threadIdx.x == 0)
     __hip_atomic_fetch_or(&p.hdr->status, kStatusState, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const float4* o = reinterpret_cast<const float4*>(p.O + r * H);
+  const int64_t orow = p.hdr->fcompact ? (int64_t)p.finv[r] : r;  // O is indexed by the forward's row order
+  const float4* o = reinterpret_cast<const float4*>(p.O + orow * H);
   const u16* w = p.W + (valid ? y : 0) * H;
   float4* d = reinterpret_cast<float4*>(p.dh + r * H);
   for (int64_t c = threadIdx.x; c < H / 4; c += 256) {
@@ -885,8 +955,24 @@ hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream
   return hipGetLastError();
 }
 
+hipError_t launch_permute(const BwdArgs& a, int* cnt, hipStream_t st) {
+  const int nchunks = (int)((a.L + 1023) / 1024);
+  hipLaunchKernelGGL(k_count_chunks, dim3((unsigned)nchunks), dim3(256), 0, st, a.labels, a.L, a.V, a.ignore_index, cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_permute_rows, dim3((unsigned)nchunks), dim3(1024), 0, st, a.labels, a.L, a.V, a.ignore_index,
+                     (const int*)cnt, nchunks, a.hdr, a.fperm, a.finv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gather_perm, dim3((unsigned)a.L), dim3(256), 0, st, a.h, a.H, (const WsHeader*)a.hdr,
+                     (const int*)a.fperm, a.hp);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose_dw_rows(const BwdArgs& a, void* hT, hipStream_t st) {
-  dim3 grid((unsigned)((a.L + 63) / 64), (unsigned)(a.H / 64));
+  // every 64-row tile up to the 128-row padding: the rows past the swept ones
+  // must be written (as zeros), the dW pass's contraction reads them
+  dim3 grid((unsigned)(a.Lpad / 64), (unsigned)(a.H / 64));
   hipLaunchKernelGGL(k_transpose_dw_rows, grid, dim3(256), 0, st, a.h, (const u16*)a.ch, a.L, a.H,
                      (const WsHeader*)a.hdr, (u16*)hT);
   return hipGetLastError();

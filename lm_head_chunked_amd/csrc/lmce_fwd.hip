@@ -209,9 +209,11 @@ __global__ __launch_bounds__(256) void k_fwd_rows(FwdArgs p, float* __restrict__
         for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
       }
       if (lane == 0) {
+        // the training forward may have run the rows in a labelled-first order
+        const int64_t pos = (p.finv != nullptr && p.hdr->fcompact) ? (int64_t)p.finv[r] : r;
         float m = kNegBig, s = 0.f;
         for (int seg = 0; seg < p.segments; ++seg)
-          lse_merge(m, s, p.part_m[(int64_t)seg * p.L + r], p.part_s[(int64_t)seg * p.L + r]);
+          lse_merge(m, s, p.part_m[(int64_t)seg * p.L + pos], p.part_s[(int64_t)seg * p.L + pos]);
         const float lse = m + logf(s);
         lse_out[r] = lse;
         nll = valid ? lse - dot : 0.f;

@@ -26,7 +26,9 @@ struct WsHeader {
   int saved;     // kSavedTag once a training forward has filled O, else 0
   int compact;   // 1 while the dW pass runs on the compacted labelled rows (set by k_compact_rows)
   int n_compact; // rows written by that compaction (its own count of labelled rows)
-  int pad[59];
+  int fcompact;  // 1 when the training forward runs on the rows reordered labelled-first (k_permute_rows)
+  int f_n;       // labelled rows of that order (the first f_n positions)
+  int pad[57];
 };
 
 struct FwdArgs {
@@ -46,6 +48,7 @@ struct FwdArgs {
   float* part_m;        // [segments][L] running max per row and segment
   float* part_s;        // [segments][L] sum of exp(z - max) per row and segment
   float* block_sum;     // [ceil(L/64)] per-block nll sums
+  const int* finv;      // training forward: position of row r in the reordered rows (hdr->fcompact), or null
 };
 
 struct BwdArgs {
@@ -77,6 +80,13 @@ struct BwdArgs {
   float* clse;
   uint16_t* ch;
   float* dw_part;       // [group][member][256][HS] partial dW slices of the dW pass's leftover blocks
+  // Training forward on the rows reordered labelled-first (when hdr->fcompact):
+  // fperm[position] = row, finv[row] = position, hp the reordered h rows (in
+  // the h^T area, free during the forward); blocks of unlabelled rows compute
+  // lse only, and O, part_m, part_s are indexed by position.
+  int* fperm;
+  int* finv;
+  uint16_t* hp;
   float* dh;
   float* dW;
 };
@@ -90,6 +100,9 @@ hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int
 // then h^T of the rows the dW pass sweeps (compacted or all L).
 hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream_t st);
 hipError_t launch_transpose_dw_rows(const BwdArgs& a, void* hT, hipStream_t st);
+// Training forward: labelled-first order of the rows (if it saves a 256-row
+// block) and the reordered h rows.
+hipError_t launch_permute(const BwdArgs& a, int* cnt, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
 // Group-scheduled kernels: the two backward passes and the fused training forward.
 constexpr int kPassDh = 0, kPassDw = 1, kPassFwdDh = 2;

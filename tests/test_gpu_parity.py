@@ -306,6 +306,40 @@ def test_train_pair_does_not_depend_on_chunk_rows():
             assert np.array_equal(o[k], base[k]), (c, k)
 
 
+# Whatever the workspace holds before a call must not reach the results:
+# every call writes all the workspace it reads (a row of h^T past L left
+# unwritten once turned into NaN in dW, 0 * NaN, with a NaN-filled
+# workspace).  Shapes with L % 128 in (0, 64], ignored rows (compaction on
+# and off), 128- and 256-wide slices.
+FILLED = [
+    (2741, 256, 3237, 0.05),
+    (700, 3072, 3000, 0.3),
+    (321, 128, 5000, 0.5),
+    (1000, 512, 900, 0.0),
+]
+
+
+@pytest.mark.parametrize("train", [False, True], ids=["plain", "train"])
+@pytest.mark.parametrize("L,H,V,ign", FILLED)
+def test_workspace_contents_do_not_matter(L, H, V, ign, train):
+    say(f"[case] NaN-filled workspace L={L} H={H} V={V} ignore={ign} train={train}")
+    h, W, y = synth.random_case(L, H, V, seed=L + 2 * V, w_std=0.05, ignore_frac=ign)
+    dev = torch.device("cuda:0")
+    hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
+    fwd, bwd = (lm.lmce_fwd_train, lm.lmce_bwd_train) if train else (lm.lmce_fwd, lm.lmce_bwd)
+    outs = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((lm.lmce_workspace_size(L, H, V, 256),), fill, dtype=torch.uint8, device=dev)
+        loss, lse = fwd(hd, Wd, yd, -100, 256, ws)
+        dh, dW = bwd(hd, Wd, yd, lse, None, -100, 256, ws)
+        assert lm.lmce_read_status(ws) == _lib.LMCE_OK
+        outs.append((float(loss), lse.cpu().numpy(), dh.cpu().numpy(), dW.cpu().numpy()))
+    assert np.isfinite(outs[1][0]) and all(np.isfinite(x).all() for x in outs[1][1:])
+    assert outs[0][0] == outs[1][0]
+    for a, b in zip(outs[0][1:], outs[1][1:]):
+        assert np.array_equal(a, b)
+
+
 def test_deterministic():
     say("[case] determinism tiny")
     h, W, y = synth.make("tiny")
