@@ -172,7 +172,11 @@ __device__ __forceinline__ void lds_wait_frags(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB
 // next stages in flight (two 64 KiB stages of a 256 x 256 tile, three 48 KiB
 // stages of a 256 x 128 one); one barrier per 64-wide K step.  Whole-line
 // (128-byte) row segments per stage matter on gfx950: with 64-byte segments
-// the same tiles ran 10 % (256 x 256) and 25 % (256 x 128) slower.
+// the same tiles ran 10 % (256 x 256) and 25 % (256 x 128) slower.  Two-stage
+// tiles with fragment prefetch place every fragment read and DMA instruction
+// between two MFMAs and pass the K-step barrier before the last sub-step's
+// MFMAs (run_interleaved): 6 to 7 % faster in both passes of the training
+// pair than issuing them in bursts after the barrier (run_staged).
 //
 // Operand addressing (bytes from the resource base): row r, K index k is at
 //   linear  (KT == 0):  r * ld + col + 2k
@@ -214,6 +218,12 @@ struct TileGemm {
 
   __device__ __forceinline__ static void run(const Operand& a, const Operand& b, int K, char* lds,
                                              f32x16 (&acc)[MB][NB]) {
+    if constexpr (PF && STAGES == 2) run_interleaved(a, b, K, lds, acc);
+    else run_staged(a, b, K, lds, acc);
+  }
+
+  __device__ __forceinline__ static void run_staged(const Operand& a, const Operand& b, int K, char* lds,
+                                                    f32x16 (&acc)[MB][NB]) {
     const int lane = lane_id();
     const int wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
@@ -285,6 +295,110 @@ struct TileGemm {
         }
       }
     }
+  }
+  // ---- interleaved schedule (two stages, fragment prefetch)
+  static constexpr int LA = BM / 8 / NW, LB = BN / 8 / NW;  // DMA instructions per wave: A rows, B rows
+
+  // One LDS-DMA instruction of stage kt: idx < LA moves 8 rows of A, else 8 rows of B (the same rows and
+  // slots as issue()).
+  __device__ __forceinline__ static void issue_one(int kt, int idx, const Operand& a, const Operand& b, char* lds,
+                                                   int wave, int lane) {
+    char* st = lds + (kt % STAGES) * STAGE_BYTES;
+    if (idx < LA) {
+      const int r0 = (wave * LA + idx) * 8;
+      const int r = r0 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      const uint32_t voff = (uint32_t)r * a.ld + k_offset<KTA>(a, kt) + (uint32_t)c * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a.rs, LMCE_LDS_PTR(st + r0 * 128), 16, voff, 0, 0, AUXA);
+    } else {
+      const int r0 = (wave * LB + idx - LA) * 8;
+      const int r = r0 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      const uint32_t voff = (uint32_t)r * b.ld + k_offset<KTB>(b, kt) + (uint32_t)c * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b.rs, LMCE_LDS_PTR(st + BM * 128 + r0 * 128), 16, voff, 0, 0, 0);
+    }
+  }
+
+  // Fragment j of sub-step ks of a stage: j < MB is A block j, else B block j - MB.
+  __device__ __forceinline__ static bf16x8 frag_j(const char* st, int j, int ks, int wm, int wn, int lane) {
+    const int c = 2 * ks + (lane >> 5);
+    if (j < MB) return stage_frag(st, wm * (BM / WM) + j * 32 + (lane & 31), c);
+    return stage_frag(st + BM * 128, wn * (BN / WN) + (j - MB) * 32 + (lane & 31), c);
+  }
+
+  __device__ __forceinline__ static void set_frag(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB], int j, bf16x8 v) {
+    if (j < MB) fa[j] = v;
+    else fb[j - MB] = v;
+  }
+
+  // One K step over stage kt.  On entry the fragments of sub-step 0 are in
+  // flight into set 0.  Each sub-step waits for its own fragments, then issues
+  // its MFMAs one at a time with one other instruction after each (scheduling
+  // barriers keep that order): the next sub-step's fragment reads, and in the
+  // last sub-step the first fragments of stage kt+1 and the DMA of stage kt+2.
+  // Before the last sub-step's MFMAs the wave has read all of stage kt, waits
+  // for its own part of stage kt+1 and passes the workgroup barrier, after
+  // which stage kt+1 is complete and stage kt's buffer can be refilled.
+  template <bool NEXT, bool DMA>
+  __device__ __forceinline__ static void step_interleaved(int kt, const Operand& a, const Operand& b, char* lds,
+                                                          int wave, int lane, int wm, int wn, bf16x8 (&fa)[2][MB],
+                                                          bf16x8 (&fb)[2][NB], f32x16 (&acc)[MB][NB]) {
+    const char* st = lds + (kt % STAGES) * STAGE_BYTES;
+    const char* nx = lds + ((kt + 1) % STAGES) * STAGE_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int cur = ks & 1;
+      lds_wait_frags_n<0>(fa[cur], fb[cur]);
+      if (NEXT && ks == NKS - 1) {
+        wait_vmcnt<0>();
+        raw_barrier();
+      }
+#pragma unroll
+      for (int i = 0; i < MB * NB; ++i) {
+        acc[i / NB][i % NB] = mfma32(fa[cur][i / NB], fb[cur][i % NB], acc[i / NB][i % NB]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < NKS) {
+          if (i < MB + NB) set_frag(fa[cur ^ 1], fb[cur ^ 1], i, frag_j(st, i, ks + 1, wm, wn, lane));
+        } else if (NEXT) {
+          if (i < MB + NB) set_frag(fa[cur ^ 1], fb[cur ^ 1], i, frag_j(nx, i, 0, wm, wn, lane));
+          if (DMA && i < LA + LB) issue_one(kt + 2, i, a, b, lds, wave, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // Two stages in LDS; stage kt+2 is loaded while stage kt+1 waits and stage
+  // kt is multiplied, and no wave waits for LDS reads with its MFMA queue
+  // empty at a stage boundary.  Same products in the same order as
+  // run_staged(), so the results are bitwise identical.
+  __device__ __forceinline__ static void run_interleaved(const Operand& a, const Operand& b, int K, char* lds,
+                                                         f32x16 (&acc)[MB][NB]) {
+    static_assert(STAGES == 2 && NKS % 2 == 0 && MB * NB >= MB + NB && MB * NB >= LA + LB,
+                  "every fragment read and DMA instruction needs an MFMA slot");
+    const int lane = lane_id(), wave = wave_id();
+    const int wm = wave / WN, wn = wave % WN;
+    const int nk = K / BK;
+    // as in run_staged(): earlier readers of this LDS are past the barrier
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    raw_barrier();
+    if (nk <= 0) return;
+    issue(0, a, b, lds, wave, lane);
+    if (nk > 1) {
+      issue(1, a, b, lds, wave, lane);
+      wait_vmcnt<LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    raw_barrier();
+    bf16x8 fa[2][MB], fb[2][NB];
+#pragma unroll
+    for (int j = 0; j < MB + NB; ++j) set_frag(fa[0], fb[0], j, frag_j(lds, j, 0, wm, wn, lane));
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) step_interleaved<true, true>(kt, a, b, lds, wave, lane, wm, wn, fa, fb, acc);
+    if (kt + 1 < nk) step_interleaved<true, false>(kt++, a, b, lds, wave, lane, wm, wn, fa, fb, acc);
+    step_interleaved<false, false>(kt, a, b, lds, wave, lane, wm, wn, fa, fb, acc);
   }
 };
 
