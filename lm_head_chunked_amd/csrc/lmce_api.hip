@@ -319,6 +319,10 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
   a.dh = dh_out;
   a.dW = dW_out;
   if (which & 1) {
+    // the dh pass's own labelled-first order, in the compaction's row array
+    // (the dW pass rewrites it afterwards) and the h^T area (filled after)
+    if (launch_permute(a, at<int>(workspace, p.off_cnt), &hdr->dcompact, a.crow, nullptr, s) != hipSuccess)
+      return LMCE_ERR_HIP;
     if (launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
     st = launch_group_pass(kPassDh, a, p, (L + 255) / 256, s);
     if (st != LMCE_OK) return st;
@@ -368,7 +372,8 @@ extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* label
   WsHeader* hdr = at<WsHeader>(workspace, 0);
   if (launch_count_labels(labels, L, V, ignore_index, hdr, kSavedTag, s) != hipSuccess) return LMCE_ERR_HIP;
   BwdArgs a = group_args(p, h, W, labels, ignore_index, workspace);
-  if (launch_permute(a, at<int>(workspace, p.off_cnt), s) != hipSuccess) return LMCE_ERR_HIP;
+  if (launch_permute(a, at<int>(workspace, p.off_cnt), &hdr->fcompact, a.fperm, a.finv, s) != hipSuccess)
+    return LMCE_ERR_HIP;
   if (launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
   st = launch_group_pass(kPassFwdDh, a, p, (L + 255) / 256, s);
   if (st != LMCE_OK) return st;

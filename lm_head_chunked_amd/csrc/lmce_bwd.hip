@@ -141,7 +141,7 @@ __global__ __launch_bounds__(1024) void k_compact_rows(const int64_t* __restrict
 // lse alone, without the O contraction.
 __global__ __launch_bounds__(1024) void k_permute_rows(const int64_t* __restrict__ labels, int64_t L, int64_t V,
                                                        int64_t ignore_index, const int* __restrict__ cnt, int nchunks,
-                                                       WsHeader* hdr, int* __restrict__ fperm, int* __restrict__ finv) {
+                                                       int* flags, int* __restrict__ fperm, int* __restrict__ finv) {
   __shared__ int scan[1024];
   __shared__ int s_before, s_total;
   if (threadIdx.x == 0) {
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(1024) void k_permute_rows(const int64_t* __restrict
   const int64_t n = s_total;
   const bool compact = (n + 255) / 256 < (L + 255) / 256;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    hdr->fcompact = compact ? 1 : 0;
-    hdr->f_n = compact ? (int)n : 0;
+    flags[0] = compact ? 1 : 0;
+    flags[1] = compact ? (int)n : 0;
   }
   if (!compact) return;
   const int64_t r = (int64_t)blockIdx.x * 1024 + threadIdx.x;
@@ -179,14 +179,14 @@ __global__ __launch_bounds__(1024) void k_permute_rows(const int64_t* __restrict
     const int64_t lab_before = s_before + scan[threadIdx.x] - f;  // labelled rows before r
     const int64_t pos = f ? lab_before : n + (r - lab_before);
     fperm[pos] = (int)r;
-    finv[r] = (int)pos;
+    if (finv) finv[r] = (int)pos;
   }
 }
 
 // h rows in the labelled-first order (one row per block), when in use.
-__global__ __launch_bounds__(256) void k_gather_perm(const u16* __restrict__ h, int64_t H, const WsHeader* hdr,
+__global__ __launch_bounds__(256) void k_gather_perm(const u16* __restrict__ h, int64_t H, const int* flags,
                                                      const int* __restrict__ fperm, u16* __restrict__ hp) {
-  if (hdr->fcompact == 0) return;
+  if (flags[0] == 0) return;
   const int64_t src = fperm[blockIdx.x];
   const uint4* in = reinterpret_cast<const uint4*>(h + src * H);
   uint4* out = reinterpret_cast<uint4*>(hp + (int64_t)blockIdx.x * H);
@@ -401,6 +401,27 @@ __device__ __forceinline__ void gstage_flush(const char* lds, rsrc_t rslot, int 
 // [256 tokens][K].  Then every member accumulates
 //   dh[rows][c0 .. c0+HS] += slot[256][K] * W^T[c0 .. c0+HS][round's vocabulary]
 // with K = 128 * (K-tiles in the round).
+// Writes an accumulator tile of TileGemm's layout (rows row0 + ..., columns
+// col0 + ...) whose tile rows are positions pos0 + ... of a row order:
+// position pos goes to dh row perm[pos], columns c0 + ...; positions at or
+// past L are skipped.  ZERO writes zeros instead (acc is not read).
+template <int MB, int NB, bool ZERO>
+__device__ __forceinline__ void store_rows_perm(float* dh, const int* perm, int64_t pos0, int64_t L, int64_t H,
+                                                int64_t c0, const f32x16 (&acc)[MB][NB], int row0, int col0, int lane) {
+  const int lrow = (lane >> 5) << 2;  // row offset of this lane half
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int reg = 0; reg < 16; ++reg) {
+      const int64_t pos = pos0 + row0 + mb * 32 + ((reg >> 2) << 3) + (reg & 3) + lrow;
+      if (pos < L) {
+        float* d = dh + (int64_t)perm[pos] * H + c0 + col0 + (lane & 31);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) d[nb * 32] = ZERO ? 0.f : acc[mb][nb][reg];
+      }
+    }
+}
+
 template <int HS>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   using P = typename BwdCfg<HS>::P;
@@ -425,24 +446,37 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   const int nrb = (int)((L + 255) / 256);
   const int n_valid = p.hdr->n_valid;
   const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
+  // Rows in this pass's labelled-first order when it saves a block
+  // (crow[position] = row, h rows in hp): blocks past the labelled rows only
+  // write their zero dh rows, and every row is read and written through the
+  // order.  Each row's products and their order stay the same.
+  const bool reordered = p.hdr->dcompact != 0;
+  const int64_t n_lab = reordered ? (int64_t)p.hdr->d_n : L;
+  const u16* const hrows = reordered ? p.hp : p.h;
   unsigned epoch = 0;
 
   for (int rb = g; rb < nrb; rb += p.n_groups) {
     const int64_t r0 = (int64_t)rb * 256;
     const int64_t rend = min(r0 + 256, L);
+    if (r0 >= n_lab) {  // (the whole group skips the block: the same rb for every member)
+      f32x16 none[C::MB][C::NB];
+      store_rows_perm<C::MB, C::NB, true>(p.dh, p.crow, r0, L, H, c0, none, wm * 64, wn * (HS / 2), lane);
+      continue;
+    }
     // producer wave (wm: vocabulary quarter, wn: token half); lane's 4 tokens
     float lse2[4], scale[4];
     int lab[4];  // label, or -2^30 for rows that take no gradient
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int64_t t = r0 + wn * 128 + nb * 32 + (lane & 31);
-      const int64_t y = t < rend ? p.labels[t] : p.ignore_index;
+      const int64_t src = t < rend ? (reordered ? (int64_t)p.crow[t] : t) : 0;
+      const int64_t y = t < rend ? p.labels[src] : p.ignore_index;
       const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
       lab[nb] = valid ? (int)y : -(1 << 30);
       scale[nb] = valid ? gscale : 0.f;
-      lse2[nb] = t < rend ? p.lse[t] * kLog2e : INFINITY;  // rows past L: probability 0
+      lse2[nb] = t < rend ? p.lse[src] * kLog2e : INFINITY;  // rows past L: probability 0
     }
-    const Operand oh = linear_operand(p.h + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
+    const Operand oh = linear_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
 
     f32x16 dacc[C::MB][C::NB];
     if constexpr (!kPark) zero_acc(dacc);
@@ -502,9 +536,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
     if constexpr (kPark) {
       f32x16 fin[C::MB][C::NB];
       unpark_acc(fin, park, wave, lane);
-      store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
+      if (reordered) store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, fin, wm * 64, wn * (HS / 2), lane);
+      else store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
     } else {
-      store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
+      if (reordered) store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, dacc, wm * 64, wn * (HS / 2), lane);
+      else store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
     }
   }
 }
@@ -955,17 +991,17 @@ hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const BwdArgs& a, int* cnt, hipStream_t st) {
+hipError_t launch_permute(const BwdArgs& a, int* cnt, int* flags, int* perm, int* inv, hipStream_t st) {
   const int nchunks = (int)((a.L + 1023) / 1024);
   hipLaunchKernelGGL(k_count_chunks, dim3((unsigned)nchunks), dim3(256), 0, st, a.labels, a.L, a.V, a.ignore_index, cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_permute_rows, dim3((unsigned)nchunks), dim3(1024), 0, st, a.labels, a.L, a.V, a.ignore_index,
-                     (const int*)cnt, nchunks, a.hdr, a.fperm, a.finv);
+                     (const int*)cnt, nchunks, flags, perm, inv);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gather_perm, dim3((unsigned)a.L), dim3(256), 0, st, a.h, a.H, (const WsHeader*)a.hdr,
-                     (const int*)a.fperm, a.hp);
+  hipLaunchKernelGGL(k_gather_perm, dim3((unsigned)a.L), dim3(256), 0, st, a.h, a.H, (const int*)flags,
+                     (const int*)perm, a.hp);
   return hipGetLastError();
 }
 

@@ -28,7 +28,9 @@ struct WsHeader {
   int n_compact; // rows written by that compaction (its own count of labelled rows)
   int fcompact;  // 1 when the training forward runs on the rows reordered labelled-first (k_permute_rows)
   int f_n;       // labelled rows of that order (the first f_n positions)
-  int pad[57];
+  int dcompact;  // 1 when the dh pass of lmce_bwd / lmce_bwd_dh runs on its own labelled-first order
+  int d_n;       // labelled rows of that order
+  int pad[55];
 };
 
 struct FwdArgs {
@@ -74,7 +76,9 @@ struct BwdArgs {
   WsHeader* hdr;
   // The labelled rows in order (written by k_compact_rows when hdr->compact):
   // their index, label and lse, and their h rows in the W^T area (free
-  // during the dW pass); the dW pass then sweeps hdr->n_valid rows.
+  // during the dW pass); the dW pass then sweeps hdr->n_valid rows.  Before
+  // that, crow holds the dh pass's labelled-first order when hdr->dcompact
+  // (crow[position] = row, h rows in hp).
   int* crow;
   int64_t* clab;
   float* clse;
@@ -100,9 +104,12 @@ hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int
 // then h^T of the rows the dW pass sweeps (compacted or all L).
 hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream_t st);
 hipError_t launch_transpose_dw_rows(const BwdArgs& a, void* hT, hipStream_t st);
-// Training forward: labelled-first order of the rows (if it saves a 256-row
-// block) and the reordered h rows.
-hipError_t launch_permute(const BwdArgs& a, int* cnt, hipStream_t st);
+// Labelled-first order of the rows, if it saves a 256-row block: flags[0] = 1
+// and flags[1] = labelled rows (else 0, 0), perm[position] = row, inv[row] =
+// position (inv may be null), and the reordered h rows in a.hp.  Used by the
+// training forward (fperm, finv, hdr->fcompact) and by the dh pass (crow,
+// hdr->dcompact).
+hipError_t launch_permute(const BwdArgs& a, int* cnt, int* flags, int* perm, int* inv, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
 // Group-scheduled kernels: the two backward passes and the fused training forward.
 constexpr int kPassDh = 0, kPassDw = 1, kPassFwdDh = 2;
