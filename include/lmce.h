@@ -148,7 +148,9 @@ int lmce_bwd_dW(const void* h, const void* W, const int64_t* labels, const float
  * lmce_bwd_train: arguments and outputs as lmce_bwd.  It must follow an
  *   lmce_fwd_train on the same inputs, workspace and stream, with no other
  *   lmce_fwd in between; otherwise dh_out is NaN and lmce_read_status()
- *   returns LMCE_ERR_STATE.
+ *   returns LMCE_ERR_STATE.  Calls of lmce_bwd, lmce_bwd_dh or lmce_bwd_dW
+ *   on the workspace in between, with any inputs, are allowed: they leave
+ *   the training forward's state alone.
  */
 int lmce_fwd_train(const void* h, const void* W, const int64_t* labels,
                    int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,

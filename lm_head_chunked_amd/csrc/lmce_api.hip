@@ -409,6 +409,10 @@ extern "C" int lmce_bwd_train(const void* h, const void* W, const int64_t* label
   if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  // N from these labels: a plain backward with other labels may have run on
+  // the workspace since the training forward (the forward's tag stays)
+  if (launch_count_labels(labels, L, V, ignore_index, at<WsHeader>(workspace, 0), -1, s) != hipSuccess)
+    return LMCE_ERR_HIP;
   BwdArgs a = group_args(p, h, W, labels, ignore_index, workspace);
   a.lse = lse;
   a.grad_loss = grad_loss;

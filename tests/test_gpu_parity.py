@@ -340,6 +340,33 @@ def test_workspace_contents_do_not_matter(L, H, V, ign, train):
         assert np.array_equal(a, b)
 
 
+def test_plain_backward_between_train_calls_leaves_the_saved_forward():
+    """A plain backward with other labels between lmce_fwd_train and
+    lmce_bwd_train on one workspace: the plain dh pass keeps its own row order
+    and flags, so the training backward still finds the forward's state.  Both
+    label sets drop enough rows that each order is in use."""
+    L, H, V = 1500, 512, 3000
+    say(f"[case] plain backward between the training calls L={L} H={H} V={V}")
+    h, W, y = synth.random_case(L, H, V, seed=91, w_std=0.05, ignore_frac=0.4)
+    _, _, y2 = synth.random_case(L, H, V, seed=92, w_std=0.05, ignore_frac=0.6)
+    dev = torch.device("cuda:0")
+    hd, Wd, yd, y2d = h.to(dev), W.to(dev), y.to(dev), y2.to(dev)
+    ws = torch.empty(lm.lmce_workspace_size(L, H, V, 256), dtype=torch.uint8, device=dev)
+    loss, lse = lm.lmce_fwd_train(hd, Wd, yd, -100, 256, ws)
+    dh_ref, dW_ref = lm.lmce_bwd_train(hd, Wd, yd, lse, None, -100, 256, ws)
+    ref = (dh_ref.cpu().numpy(), dW_ref.cpu().numpy())
+    loss, lse = lm.lmce_fwd_train(hd, Wd, yd, -100, 256, ws)
+    _, lse2 = lm.lmce_fwd(hd, Wd, y2d, -100, 256, torch.empty_like(ws))
+    dh2, dW2 = lm.lmce_bwd(hd, Wd, y2d, lse2, None, -100, 256, ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, None, -100, 256, ws)
+    assert lm.lmce_read_status(ws) == _lib.LMCE_OK
+    assert np.array_equal(dh.cpu().numpy(), ref[0]) and np.array_equal(dW.cpu().numpy(), ref[1])
+    # and the plain backward itself, on the other labels
+    r2 = oracle.fwd_bwd(h.float().numpy(), W.float().numpy(), y2.numpy())
+    assert rel_fro(dh2.cpu().numpy(), r2["dh"]) <= 1e-2 and rel_fro(dW2.cpu().numpy(), r2["dW"]) <= 1e-2
+    assert np.all(dh2.cpu().numpy()[(y2 == -100).numpy()] == 0.0)
+
+
 def test_deterministic():
     say("[case] determinism tiny")
     h, W, y = synth.make("tiny")
