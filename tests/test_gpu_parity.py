@@ -367,6 +367,27 @@ def test_plain_backward_between_train_calls_leaves_the_saved_forward():
     assert np.all(dh2.cpu().numpy()[(y2 == -100).numpy()] == 0.0)
 
 
+@pytest.mark.parametrize("L,H,V,ign", [(1300, 384, 2100, 0.45), (600, 3072, 1500, 0.6)])
+def test_backward_halves_match_the_whole(L, H, V, ign):
+    """lmce_bwd_dh and lmce_bwd_dW give bitwise the dh and dW of lmce_bwd, with
+    enough ignored rows that the dh pass runs on its labelled-first order."""
+    say(f"[case] backward halves L={L} H={H} V={V} ignore={ign}")
+    h, W, y = synth.random_case(L, H, V, seed=L + V, w_std=0.05, ignore_frac=ign)
+    dev = torch.device("cuda:0")
+    hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
+    ws = torch.empty(lm.lmce_workspace_size(L, H, V, 256), dtype=torch.uint8, device=dev)
+    _, lse = lm.lmce_fwd(hd, Wd, yd, -100, 256, ws)
+    dh, dW = lm.lmce_bwd(hd, Wd, yd, lse, None, -100, 256, ws)
+    dh1 = lm.lmce_bwd_dh(hd, Wd, yd, lse, None, -100, 256, ws)
+    dW1 = lm.lmce_bwd_dW(hd, Wd, yd, lse, None, -100, 256, ws)
+    assert lm.lmce_read_status(ws) == _lib.LMCE_OK
+    assert np.array_equal(dh1.cpu().numpy(), dh.cpu().numpy())
+    assert np.array_equal(dW1.cpu().numpy(), dW.cpu().numpy())
+    ref = oracle.fwd_bwd(h.float().numpy(), W.float().numpy(), y.numpy())
+    assert rel_fro(dh1.cpu().numpy(), ref["dh"]) <= 1e-2 and rel_fro(dW1.cpu().numpy(), ref["dW"]) <= 1e-2
+    assert np.all(dh1.cpu().numpy()[(y == -100).numpy()] == 0.0)
+
+
 def test_deterministic():
     say("[case] determinism tiny")
     h, W, y = synth.make("tiny")
