@@ -73,34 +73,57 @@ def recorded_traffic(workload, kernel):
     return int(m.group(1)) if m else None
 
 
+def host_cores():
+    """(threads the oracle may use, nproc, CPU model): every core this process
+    may run on, capped by the thread share the host grants (OMP_NUM_THREADS)."""
+    nproc = os.cpu_count() or 1
+    allowed = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(allowed, int(share)) if share.isdigit() and int(share) > 0 else allowed
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, nproc, model
+
+
 def cpu_baseline(wl, W_cpu, h_rows, y_rows, n_valid):
-    """fp64 oracle on the first rows of the workload at full H and V.
+    """fp64 oracle on the first rows of the workload at full H and V, with
+    its BLAS on every host core this process may use.
 
     Returns the timing record and the oracle's result for those rows.  Every
     row's lse depends on that row alone and its dh on the row and the
     workload's count N of rows with a label, so the upstream gradient
     n_sub / N (n_sub: labelled rows of the sample) makes the oracle's dh rows
     those of the whole workload."""
-    import numpy as np
     import threadpoolctl
 
     import oracle
 
+    threads, nproc, model = host_cores()
     h_np = h_rows.float().numpy()
     y_np = y_rows.numpy()
     W_np = W_cpu.float().numpy()
-    oracle.forward(h_np[:8], W_np, y_np[:8])  # warm BLAS
-    n_sub = int((y_np != -100).sum())
-    grad = n_sub / n_valid if n_sub > 0 and n_valid > 0 else 1.0
-    t0 = time.perf_counter()
-    ref = oracle.fwd_bwd(h_np, W_np, y_np, grad=grad)
-    dt = time.perf_counter() - t0
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [os.cpu_count()])
+    with threadpoolctl.threadpool_limits(limits=threads, user_api="blas"):
+        oracle.forward(h_np[:8], W_np, y_np[:8])  # warm BLAS
+        n_sub = int((y_np != -100).sum())
+        grad = n_sub / n_valid if n_sub > 0 and n_valid > 0 else 1.0
+        t0 = time.perf_counter()
+        ref = oracle.fwd_bwd(h_np, W_np, y_np, grad=grad)
+        dt = time.perf_counter() - t0
+        used = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(used or [threads])
     n = h_np.shape[0]
-    info = {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    info = {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "nproc": nproc,
+            "cpu_model": model,
             "sample": f"first {n} rows of {wl.name} at full H={wl.H}, V={wl.V}: fp64 forward+backward in "
-                      f"{dt:.2f} s (full workload extrapolates to {wl.L / n * dt:.0f} s)"}
+                      f"{dt:.2f} s on {cores} BLAS threads (host: {nproc} CPUs, {model}); "
+                      f"the full workload extrapolates to {wl.L / n * dt:.0f} s"}
     return info, ref
 
 
@@ -111,7 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen3_8b_1m_shard")
     ap.add_argument("--chunk-rows", type=int, default=None)
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="rows of the CPU-baseline sample (about 10-30 s of oracle work at the default workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pair", choices=["train", "plain"], default="train",
                     help="train: lmce_fwd_train + lmce_bwd_train; plain: lmce_fwd + lmce_bwd_dh + lmce_bwd_dW")
@@ -269,6 +293,12 @@ def main():
                             "within_tol": bool(e_lse <= 2e-3 and e_dh <= 1e-2)}
         log(f"[bench] parity on {n_rows} rows: lse max abs err {e_lse:.2e}, dh rel err {e_dh:.2e}")
     print(json.dumps(result), flush=True)
+    # Release device memory and let queued work drain before the interpreter
+    # exits, so that no device state is torn down by exit-time destructors
+    # while a profiler's own finalisation runs.
+    del h, W, y, loss, lse, g
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -163,12 +163,23 @@ int lmce_bwd_train(const void* h, const void* W, const int64_t* labels, const fl
 
 /*
  * Synchronises `stream` and returns the asynchronous status recorded in the
- * workspace by the last calls on it: LMCE_OK, LMCE_ERR_LABEL, LMCE_ERR_STATE,
- * or LMCE_ERR_HIP if the synchronisation failed or a group-scheduled
- * workgroup gave up waiting for the other members of its group (a bounded
- * wait; the results are then incomplete).
+ * workspace by every call on it since the previous lmce_read_status (the
+ * flags of the calls accumulate; a later call never erases an earlier
+ * call's error), then clears those flags:
+ *   LMCE_ERR_LABEL  a label was outside [0, V) and not ignore_index;
+ *   LMCE_ERR_HIP    the synchronisation failed, or a group-scheduled
+ *                   workgroup gave up waiting for the other members of its
+ *                   group (a bounded wait; that call's results are then
+ *                   incomplete: its loss is NaN, and after such an
+ *                   lmce_fwd_train the following lmce_bwd_train writes a NaN
+ *                   dh);
+ *   LMCE_ERR_STATE  an lmce_bwd_train found no complete training forward;
+ *   LMCE_OK         none of these.
+ * With several flags set, the first in this list is returned.  A workspace
+ * on which no call has run reads LMCE_OK.  Not to be called while other
+ * calls on the workspace are in flight on another stream.
  */
-int lmce_read_status(const void* workspace, void* stream);
+int lmce_read_status(void* workspace, void* stream);
 
 #ifdef __cplusplus
 }

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "lmce.h"
@@ -16,6 +17,18 @@ namespace {
 constexpr int64_t kMaxRows = int64_t(1) << 21;   // L and V limits (32-bit buffer offsets stay exact)
 constexpr int64_t kMaxHidden = 16384;
 constexpr int kSpinLimit = 1 << 21;                // bound of every group wait (about a second)
+
+// Bound of every group wait.  LMCE_SPIN_LIMIT (a non-negative integer) lowers
+// it, so that tests can make the waits give up and check how that failure is
+// reported while every kernel still exits normally.
+int spin_limit() {
+  const char* e = getenv("LMCE_SPIN_LIMIT");
+  if (e == nullptr || *e == '\0') return kSpinLimit;
+  char* end = nullptr;
+  const long v = strtol(e, &end, 10);
+  if (end == e || *end != '\0' || v < 0 || v > kSpinLimit) return kSpinLimit;
+  return (int)v;
+}
 
 struct Plan {
   int64_t L, H, V;
@@ -269,7 +282,7 @@ BwdArgs group_args(const Plan& p, const void* h, const void* W, const int64_t* l
   a.ignore_index = ignore_index;
   a.Lpad = p.Lpad;
   a.Vpad = p.Vpad;
-  a.spin_limit = kSpinLimit;
+  a.spin_limit = spin_limit();
   a.sync = at<unsigned>(workspace, p.off_sync);
   a.xbuf = at<uint16_t>(workspace, p.off_xbuf);
   a.park = at<float>(workspace, p.off_park);
@@ -369,8 +382,10 @@ extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* label
   if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  // the saved tag is cleared now and set by the forward's last kernel only
+  // if every group wait of k_fwd_dh succeeded
   WsHeader* hdr = at<WsHeader>(workspace, 0);
-  if (launch_count_labels(labels, L, V, ignore_index, hdr, kSavedTag, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (launch_count_labels(labels, L, V, ignore_index, hdr, 0, s) != hipSuccess) return LMCE_ERR_HIP;
   BwdArgs a = group_args(p, h, W, labels, ignore_index, workspace);
   if (launch_permute(a, at<int>(workspace, p.off_cnt), &hdr->fcompact, a.fperm, a.finv, s) != hipSuccess)
     return LMCE_ERR_HIP;
@@ -393,7 +408,7 @@ extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* label
   f.part_s = a.part_s;
   f.block_sum = at<float>(workspace, p.off_bsum);
   f.finv = a.finv;
-  if (launch_fwd_rows(f, loss_out, lse_out, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (launch_fwd_rows(f, loss_out, lse_out, s, true) != hipSuccess) return LMCE_ERR_HIP;
   return LMCE_OK;
 }
 
@@ -422,11 +437,18 @@ extern "C" int lmce_bwd_train(const void* h, const void* W, const int64_t* label
   return dw_pass(a, p, workspace, s);
 }
 
-extern "C" int lmce_read_status(const void* workspace, void* stream) {
+extern "C" int lmce_read_status(void* workspace, void* stream) {
   if (!aligned(workspace, 256)) return LMCE_ERR_NULL;
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return LMCE_ERR_HIP;
   WsHeader hdr;
   if (hipMemcpy(&hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost) != hipSuccess) return LMCE_ERR_HIP;
+  if (hdr.tag != kHdrTag) return LMCE_OK;  // no call has run on this workspace yet
+  if (hdr.status != 0) {
+    // the flags accumulate over calls until read here; clear them
+    const int zero = 0;
+    if (hipMemcpy(&at<WsHeader>(workspace, 0)->status, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+      return LMCE_ERR_HIP;
+  }
   if (hdr.status & kStatusLabel) return LMCE_ERR_LABEL;
   if (hdr.status & kStatusSync) return LMCE_ERR_HIP;
   if (hdr.status & kStatusState) return LMCE_ERR_STATE;

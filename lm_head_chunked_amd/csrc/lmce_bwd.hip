@@ -307,7 +307,10 @@ __device__ __forceinline__ bool group_arrive_wait(unsigned* ctr, unsigned target
         break;
       }
     }
-    if (!ok) __hip_atomic_fetch_or(&hdr->status, kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!ok) {
+      __hip_atomic_fetch_or(&hdr->status, kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(&hdr->call_flags, kStatusSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     *s_flag = ok;
   }
   __syncthreads();
@@ -940,7 +943,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
 }
 
 // dh = g/N * (O - W_y) for rows with a label, 0 for the others; NaN (and the
-// state flag) if the workspace does not hold a training forward's O.
+// state flag) if the workspace does not hold a complete training forward's O
+// (none ran, another forward ran since, or one of its group waits gave up).
 __global__ __launch_bounds__(256) void k_dh_finish(BwdArgs p) {
   const int64_t r = blockIdx.x;
   const int64_t H = p.H;

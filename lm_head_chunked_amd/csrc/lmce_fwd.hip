@@ -18,7 +18,10 @@
 namespace lmce {
 
 // Counts rows whose label is not ignore_index and checks that the others lie
-// in [0, V).  One workgroup; fixed-order reduction.
+// in [0, V).  One workgroup; fixed-order reduction.  It is the first kernel of
+// every entry point: it clears the call's own flags, ORs a label error into
+// them and into the accumulated status (which only lmce_read_status clears),
+// and initialises the header of a workspace this library has not used yet.
 // `saved` >= 0 is written to the header's training-forward tag.
 __global__ __launch_bounds__(1024) void k_count_labels(const int64_t* __restrict__ labels, int64_t L, int64_t V,
                                                        int64_t ignore_index, WsHeader* __restrict__ hdr, int saved) {
@@ -43,8 +46,15 @@ __global__ __launch_bounds__(1024) void k_count_labels(const int64_t* __restrict
     __syncthreads();
   }
   if (threadIdx.x == 0) {
+    if (hdr->tag != kHdrTag) {  // a fresh workspace: no earlier status, no saved forward
+      hdr->status = 0;
+      hdr->saved = 0;
+      hdr->tag = kHdrTag;
+    }
+    const int flags = s_bad[0] ? kStatusLabel : 0;
     hdr->n_valid = s_cnt[0];
-    hdr->status = s_bad[0] ? kStatusLabel : 0;
+    hdr->call_flags = flags;
+    hdr->status |= flags;
     if (saved >= 0) hdr->saved = saved;
   }
 }
@@ -229,8 +239,11 @@ __global__ __launch_bounds__(256) void k_fwd_rows(FwdArgs p, float* __restrict__
   }
 }
 
-// loss = (sum of block sums, fixed order) / N; NaN if N == 0 or a label was bad.
-__global__ __launch_bounds__(256) void k_fwd_loss(FwdArgs p, int nblocks, float* __restrict__ loss_out) {
+// loss = (sum of block sums, fixed order) / N; NaN if N == 0, or if this call
+// saw a bad label or a group wait that gave up.  train: the last kernel of the
+// training forward, which marks the workspace as holding a complete O only
+// when none of its group waits gave up.
+__global__ __launch_bounds__(256) void k_fwd_loss(FwdArgs p, int nblocks, float* __restrict__ loss_out, int train) {
   __shared__ float red[256];
   float acc = 0.f;
   for (int i = threadIdx.x; i < nblocks; i += 256) acc += p.block_sum[i];
@@ -242,9 +255,11 @@ __global__ __launch_bounds__(256) void k_fwd_loss(FwdArgs p, int nblocks, float*
   }
   if (threadIdx.x == 0) {
     const int n = p.hdr->n_valid;
+    const int flags = __hip_atomic_load(&p.hdr->call_flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float loss = (n > 0) ? red[0] / (float)n : __builtin_nanf("");
-    if (p.hdr->status != 0) loss = __builtin_nanf("");
+    if (flags != 0) loss = __builtin_nanf("");
     *loss_out = loss;
+    if (train) p.hdr->saved = (flags & kStatusSync) ? 0 : kSavedTag;
   }
 }
 
@@ -265,13 +280,13 @@ hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStre
 
 // Merges the per-segment (max, sum) partials of every row into lse, forms
 // nll and the loss.
-hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st) {
+hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st, bool train) {
   hipError_t e;
   const int nblocks = (int)((a.L + 63) / 64);
   hipLaunchKernelGGL(k_fwd_rows, dim3(nblocks), dim3(256), 0, st, a, lse_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_fwd_loss, dim3(1), dim3(256), 0, st, a, nblocks, loss_out);
+  hipLaunchKernelGGL(k_fwd_loss, dim3(1), dim3(256), 0, st, a, nblocks, loss_out, train ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ constexpr int kStatusLabel = 1;     // asynchronous flag: a label was out of ran
 constexpr int kStatusSync = 2;      // asynchronous flag: a group wait timed out
 constexpr int kStatusState = 4;     // asynchronous flag: a training backward without its training forward
 constexpr int kSavedTag = 0x6c6d6365;  // header tag: the workspace holds a training forward's O
+constexpr int kHdrTag = 0x6c6d6831;    // header tag: status and saved were initialised by this library
 constexpr int kStageK = 128;        // hidden-size granularity (the backward slices H by 128)
 constexpr int kVTile = 256;         // vocabulary rows per forward logit tile
 constexpr int kSyncStride = 64;     // u32 words between two groups' counters (256 bytes)
@@ -22,16 +23,19 @@ constexpr int kXstatPerWG = 3 * 256 * 4;       // fused forward: per-member roun
 // First 256 bytes of the workspace.
 struct WsHeader {
   int n_valid;   // rows whose label is not ignore_index (and is in range)
-  int status;    // 0, or kStatusLabel | kStatusSync | kStatusState
-  int saved;     // kSavedTag once a training forward has filled O, else 0
+  int status;    // flags of every call since lmce_read_status last cleared them: kStatusLabel | kStatusSync | kStatusState
+  int saved;     // kSavedTag once a training forward has filled O without a failed group wait, else 0
   int compact;   // 1 while the dW pass runs on the compacted labelled rows (set by k_compact_rows)
   int n_compact; // rows written by that compaction (its own count of labelled rows)
   int fcompact;  // 1 when the training forward runs on the rows reordered labelled-first (k_permute_rows)
   int f_n;       // labelled rows of that order (the first f_n positions)
   int dcompact;  // 1 when the dh pass of lmce_bwd / lmce_bwd_dh runs on its own labelled-first order
   int d_n;       // labelled rows of that order
-  int pad[55];
+  int tag;       // kHdrTag once k_count_labels has initialised status and saved
+  int call_flags;  // flags raised by the current entry point only (cleared when it starts)
+  int pad[53];
 };
+static_assert(sizeof(WsHeader) == 256, "the header is the first 256 bytes of the workspace");
 
 struct FwdArgs {
   const uint16_t* h;
@@ -98,7 +102,9 @@ struct BwdArgs {
 hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int64_t ignore_index, WsHeader* hdr,
                                int saved, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
-hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
+// train: the training forward, whose last kernel sets the saved tag when its
+// group waits all succeeded.
+hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st, bool train = false);
 hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st);
 // Compaction of the labelled rows for the dW pass (cnt: ceil(L / 1024) ints),
 // then h^T of the rows the dW pass sweeps (compacted or all L).

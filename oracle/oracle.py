@@ -53,7 +53,8 @@ Parity pins: every function here is pinned by CPU tests against closed forms
 (W = 0), a brute-force high-precision evaluation at V <= 64, PyTorch's
 cross_entropy with autograd in float64, central finite differences,
 invariants (column sums of dW, vocab shifts, permutations, ignored rows) and
-a statistical sanity check.  No function in this file is "parity unpinned".
+a statistical sanity check, and the label-range check by labels outside [0, V)
+that must raise.  No function in this file is "parity unpinned".
 """
 
 from __future__ import annotations

@@ -253,6 +253,35 @@ def pin_statistics(orc):
     assert abs(out["loss"] - out["lse"].mean()) <= 0.1
 
 
+# --------------------------------------------------------------------- S5
+def pin_label_range(orc):
+    """A label that is not ignore_index must lie in [0, V): -1, any other
+    negative value and V itself are errors in every entry point (they would
+    otherwise index the logits of another class, e.g. column V - 1 for -1);
+    ignore_index itself, 0 and V - 1 are accepted."""
+    L, H, V = 6, 4, 9
+    h, W, y = _case(L, H, V, seed=16, ignore=(2,))
+    for bad in (-1, -7, V, V + 3):
+        yb = y.copy()
+        yb[4] = bad
+        for call in (lambda: orc.forward(h, W, yb), lambda: orc.backward(h, W, yb),
+                     lambda: orc.fwd_bwd(h, W, yb), lambda: orc.rows_forward(h, W, yb),
+                     lambda: orc.rows_dh(h, W, yb, 5)):
+            try:
+                call()
+            except ValueError:
+                continue
+            raise AssertionError(f"label {bad} outside [0, {V}) was accepted")
+    # the edges of the range and a custom ignore_index are fine
+    ye = y.copy()
+    ye[0], ye[1] = 0, V - 1
+    out = orc.fwd_bwd(h, W, ye)
+    assert out["n_valid"] == L - 1
+    yc = np.where(ye == IGN, -1, ye)
+    out_c = orc.fwd_bwd(h, W, yc, ignore_index=-1)
+    assert out_c["n_valid"] == L - 1 and abs(out_c["loss"] - out["loss"]) <= 1e-12
+
+
 # --------------------------------------------------------------------- subset helpers
 def pin_row_helpers(orc):
     """rows_forward / rows_dh agree with the full-array functions row by row."""
@@ -276,5 +305,6 @@ ALL_PINS = [
     pin_ignored_rows,
     pin_invariants,
     pin_statistics,
+    pin_label_range,
     pin_row_helpers,
 ]

@@ -463,14 +463,96 @@ def test_autograd_binding():
     loss = lm.chunked_nll(hd, Wd, y.to(dev))
     (loss * 0.5).backward()
     ref = oracle.fwd_bwd(np32(h), np32(W), y.numpy(), grad=0.5)
-    assert abs(float(loss) - ref["loss"]) <= LOSS_REL * abs(ref["loss"])
+    assert abs(float(loss.detach()) - ref["loss"]) <= LOSS_REL * abs(ref["loss"])
     assert rel_fro(np32(hd.grad), ref["dh"]) <= GRAD_REL
     assert rel_fro(np32(Wd.grad), ref["dW"]) <= GRAD_REL
 
 
 def test_qwen3_06b_head_full_parity():
-    say("[case] qwen3_0.6b full L=8192 H=1024 V=151936 (oracle ~30 s)")
+    """Both pairs against the full oracle at the Qwen3-0.6B head: every output."""
+    say("[case] qwen3_0.6b full L=8192 H=1024 V=151936, both pairs (oracle ~30 s)")
     h, W, y = synth.make("qwen3_0.6b")
-    gpu = run_gpu(h, W, y)
+    ref = oracle.fwd_bwd(np32(h), np32(W), y.numpy(), grad=1.25)
+    for train in (False, True):
+        gpu = run_gpu(h, W, y, grad=1.25, train=train)
+        assert_parity(gpu, ref, f"qwen3_0.6b train={train}")
+        assert np.all(gpu["dh"][(y == -100).numpy()] == 0.0)
+
+
+def _with_spin_limit(value, fn):
+    """Runs fn with the library's internal group-wait bound set to `value`
+    (read by every call from LMCE_SPIN_LIMIT); 0 makes every wait that finds
+    its group incomplete give up at once, and every kernel still exits."""
+    import os
+
+    old = os.environ.get("LMCE_SPIN_LIMIT")
+    os.environ["LMCE_SPIN_LIMIT"] = str(value)
+    try:
+        return fn()
+    finally:
+        if old is None:
+            del os.environ["LMCE_SPIN_LIMIT"]
+        else:
+            os.environ["LMCE_SPIN_LIMIT"] = old
+
+
+def test_failed_group_wait_survives_the_following_backward():
+    """A training forward whose group waits give up (forced from the host) is
+    reported by lmce_read_status after the following, clean lmce_bwd_train:
+    the flags accumulate until read.  That forward's loss is NaN, and the
+    backward, finding no complete forward, writes a NaN dh.  After the read
+    clears the flags, a clean pair passes parity again."""
+    L, H, V = 2048, 1024, 20000  # 8 row blocks, 8 members, 10 rounds of two waits
+    say(f"[case] forced group-wait failure L={L} H={H} V={V}")
+    h, W, y = synth.random_case(L, H, V, seed=31, w_std=0.05, ignore_frac=0.1)
+    dev = torch.device("cuda:0")
+    hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
+    ws = torch.empty(lm.lmce_workspace_size(L, H, V), dtype=torch.uint8, device=dev)
+    loss, lse = _with_spin_limit(0, lambda: lm.lmce_fwd_train(hd, Wd, yd, workspace=ws))
+    torch.cuda.synchronize()
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws)
+    assert lm.lmce_read_status(ws) == _lib.LMCE_ERR_HIP
+    assert math.isnan(float(loss))
+    assert torch.isnan(dh).all()
+    assert lm.lmce_read_status(ws) == _lib.LMCE_OK  # the read cleared the flags
+    loss, lse = lm.lmce_fwd_train(hd, Wd, yd, workspace=ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws)
+    assert lm.lmce_read_status(ws) == _lib.LMCE_OK
     ref = oracle.fwd_bwd(np32(h), np32(W), y.numpy())
-    assert_parity(gpu, ref, "qwen3_0.6b")
+    gpu = {"loss": float(loss), "lse": lse.cpu().numpy(), "dh": dh.cpu().numpy(), "dW": dW.cpu().numpy(),
+           "status": _lib.LMCE_OK}
+    assert_parity(gpu, ref, "after a forced wait failure")
+
+
+def test_failed_wait_in_a_backward_pass_is_reported():
+    """The plain backward's group waits give up: LMCE_ERR_HIP, then clear."""
+    L, H, V = 1024, 512, 9000
+    say(f"[case] forced group-wait failure in lmce_bwd L={L} H={H} V={V}")
+    h, W, y = synth.random_case(L, H, V, seed=32, w_std=0.05, ignore_frac=0.1)
+    dev = torch.device("cuda:0")
+    hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
+    ws = torch.empty(lm.lmce_workspace_size(L, H, V), dtype=torch.uint8, device=dev)
+    loss, lse = lm.lmce_fwd(hd, Wd, yd, workspace=ws)
+    _with_spin_limit(0, lambda: lm.lmce_bwd(hd, Wd, yd, lse, workspace=ws))
+    assert lm.lmce_read_status(ws) == _lib.LMCE_ERR_HIP
+    assert math.isfinite(float(loss))
+    assert lm.lmce_read_status(ws) == _lib.LMCE_OK
+
+
+def test_label_error_accumulates_until_read():
+    """A bad label in one call stays reported after later clean calls on the
+    same workspace; the later clean calls' own loss is not NaN."""
+    say("[case] label error, then clean calls, then one read")
+    h, W, y = synth.random_case(300, 128, 700, seed=33, ignore_frac=0.1)
+    ybad = y.clone()
+    ybad[17] = -5
+    dev = torch.device("cuda:0")
+    hd, Wd = h.to(dev), W.to(dev)
+    ws = torch.empty(lm.lmce_workspace_size(300, 128, 700), dtype=torch.uint8, device=dev)
+    loss_bad, _ = lm.lmce_fwd(hd, Wd, ybad.to(dev), workspace=ws)
+    loss, lse = lm.lmce_fwd_train(hd, Wd, y.to(dev), workspace=ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, y.to(dev), lse, workspace=ws)
+    assert lm.lmce_read_status(ws) == _lib.LMCE_ERR_LABEL
+    assert math.isnan(float(loss_bad)) and math.isfinite(float(loss))
+    assert torch.isfinite(dh).all() and torch.isfinite(dW).all()
+    assert lm.lmce_read_status(ws) == _lib.LMCE_OK

@@ -30,6 +30,9 @@ MUTATIONS = {
     "dh_uses_transposed_softmax_scale": ("dh[r0:r1] = G @ W64", "dh[r0:r1] = (G * (1.0 + 1.0 / (1 + np.arange(G.shape[1])))) @ W64"),
     "dW_missing_block": ("dW += G.T @ h64[r0:r1]", "dW = G.T @ h64[r0:r1]"),
     "grad_ignored": ("scale = float(grad) / n_valid", "scale = 1.0 / n_valid"),
+    "label_range_drops_negative": ("bad = valid & ((y < 0) | (y >= V))", "bad = valid & (y >= V)"),
+    "label_range_off_by_one_at_V": ("bad = valid & ((y < 0) | (y >= V))", "bad = valid & ((y < 0) | (y > V))"),
+    "label_range_check_removed": ("    if np.any(bad):\n", "    if False:\n"),
 }
 
 
