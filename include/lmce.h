@@ -59,7 +59,8 @@ typedef enum {
   LMCE_ERR_WORKSPACE = -4,   /* workspace_bytes smaller than lmce_workspace_size() */
   LMCE_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed */
   LMCE_ERR_LABEL = -6,       /* (asynchronous) a label is outside [0, V) and not ignore_index */
-  LMCE_ERR_STATE = -7        /* (asynchronous) lmce_bwd_train without a preceding lmce_fwd_train on the workspace */
+  LMCE_ERR_STATE = -7,       /* (asynchronous) lmce_bwd_train without a preceding lmce_fwd_train on the workspace */
+  LMCE_ERR_SCRATCH = -8      /* lmce_fwd_noalloc: the shape needs more than its fixed area holds */
 } lmce_status;
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
@@ -100,6 +101,29 @@ int lmce_fwd(const void* h, const void* W, const int64_t* labels,
              int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
              float* loss_out, float* lse_out,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lmce_fwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments (minus the workspace), same kernels
+ * and bitwise the same loss_out and lse_out as lmce_fwd.
+ *
+ * Instead of a workspace it uses a fixed area of device memory that the
+ * library holds: 65 MiB per device, reserved on each device where the
+ * library's kernels are loaded and held until the process ends.  That area
+ * has room for shapes with L <= 2^20 rows (any V and H within the limits
+ * above); larger L returns LMCE_ERR_SCRATCH before anything is enqueued.
+ * The call allocates nothing and synchronises nothing.
+ *
+ * All calls on one device share its area: calls that may overlap in time on
+ * one device (other streams, other threads) race and must be serialised by
+ * the caller.  Each call clears the area's header first, so the previous
+ * call's contents never reach the results.  A bad label makes loss_out NaN;
+ * there is no workspace for lmce_read_status here.
+ */
+int lmce_fwd_noalloc(const void* h, const void* W, const int64_t* labels,
+                     int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
+                     float* loss_out, float* lse_out, void* stream);
 
 /*
  * Backward.  Same page and sections; the gradient of the mean NLL is

@@ -29,6 +29,7 @@ __all__ = [
     "lmce_fwd_train",
     "lmce_bwd_train",
     "lmce_read_status",
+    "lmce_fwd_noalloc",
     "chunked_nll",
     "LmceError",
     "IGNORE_INDEX",
@@ -81,6 +82,21 @@ def lmce_fwd(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_R
     st = _lib.fwd(h.data_ptr(), W.data_ptr(), labels.data_ptr(), L, H, V, ignore_index, chunk_rows,
                   loss.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
     _lib.check(st, "lmce_fwd")
+    return loss, lse
+
+
+def lmce_fwd_noalloc(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS, loss_out=None,
+                     lse_out=None):
+    """lmce_fwd on the library's fixed device area instead of a workspace
+    (the C entry point allocates nothing; pass loss_out and lse_out to keep
+    this wrapper from allocating them).  Calls that overlap on one device race."""
+    L, H, V = _check_inputs(h, W, labels)
+    dev = h.device
+    loss = torch.empty((), dtype=torch.float32, device=dev) if loss_out is None else loss_out
+    lse = torch.empty(L, dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    st = _lib.fwd_noalloc(h.data_ptr(), W.data_ptr(), labels.data_ptr(), L, H, V, ignore_index, chunk_rows,
+                          loss.data_ptr(), lse.data_ptr(), _stream(dev))
+    _lib.check(st, "lmce_fwd_noalloc")
     return loss, lse
 
 

@@ -21,6 +21,7 @@ LMCE_ERR_WORKSPACE = -4
 LMCE_ERR_HIP = -5
 LMCE_ERR_LABEL = -6
 LMCE_ERR_STATE = -7
+LMCE_ERR_SCRATCH = -8
 
 # Every symbol the public header declares, with (restype, argtypes).
 _c_i64 = ctypes.c_int64
@@ -42,6 +43,8 @@ SIGNATURES = {
     "lmce_bwd_train": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                       _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_read_status": (ctypes.c_int, [_c_vp, _c_vp]),
+    "lmce_fwd_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                        _c_vp, _c_vp, _c_vp]),
 }
 
 _lib = None
@@ -118,6 +121,11 @@ def bwd_train(h_ptr, W_ptr, labels_ptr, lse_ptr, L, H, V, ignore_index, chunk_ro
               ws_bytes, stream):
     return load().lmce_bwd_train(h_ptr, W_ptr, labels_ptr, lse_ptr, int(L), int(H), int(V), int(ignore_index),
                                  int(chunk_rows), grad_ptr, dh_ptr, dW_ptr, ws_ptr, int(ws_bytes), stream)
+
+
+def fwd_noalloc(h_ptr, W_ptr, labels_ptr, L, H, V, ignore_index, chunk_rows, loss_ptr, lse_ptr, stream):
+    return load().lmce_fwd_noalloc(h_ptr, W_ptr, labels_ptr, int(L), int(H), int(V), int(ignore_index),
+                                   int(chunk_rows), loss_ptr, lse_ptr, stream)
 
 
 def read_status(ws_ptr, stream) -> int:

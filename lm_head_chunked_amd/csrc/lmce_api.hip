@@ -8,6 +8,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "lmce.h"
 #include "lmce_internal.h"
 
@@ -151,6 +153,7 @@ extern "C" const char* lmce_strerror(int status) {
     case LMCE_ERR_HIP: return "HIP runtime error";
     case LMCE_ERR_LABEL: return "a label is outside [0, V) and is not ignore_index";
     case LMCE_ERR_STATE: return "lmce_bwd_train without a preceding lmce_fwd_train on this workspace";
+    case LMCE_ERR_SCRATCH: return "the shape needs more than the fixed no-allocation area holds (L up to 2^20 rows)";
     default: return "unknown status";
   }
 }
@@ -164,28 +167,24 @@ extern "C" int lmce_workspace_size(int64_t L, int64_t H, int64_t V, int64_t chun
   return LMCE_OK;
 }
 
-extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int64_t L, int64_t H, int64_t V,
-                        int64_t ignore_index, int64_t chunk_rows, float* loss_out, float* lse_out, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  Plan p;
-  int st = make_plan(L, H, V, chunk_rows, &p);
-  if (st != LMCE_OK) return st;
-  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(labels, 8) || !aligned(loss_out, 4) || !aligned(lse_out, 4) ||
-      !aligned(workspace, 256))
-    return LMCE_ERR_NULL;
-  if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+namespace lmce {
+namespace {
 
-  WsHeader* hdr = at<WsHeader>(workspace, 0);
-  if (launch_count_labels(labels, L, V, ignore_index, hdr, 0, s) != hipSuccess) return LMCE_ERR_HIP;
+// The plain forward on a prepared area: the header at `hdr` and the
+// per-segment partials and block sums at the plan's offsets from `base`
+// (the first p.off_hT bytes of a workspace layout).
+int fwd_launch(const Plan& p, const void* h, const void* W, const int64_t* labels, int64_t ignore_index,
+               float* loss_out, float* lse_out, void* base, hipStream_t s) {
+  WsHeader* hdr = at<WsHeader>(base, 0);
+  if (launch_count_labels(labels, p.L, p.V, ignore_index, hdr, 0, s) != hipSuccess) return LMCE_ERR_HIP;
   FwdArgs a = {};
   a.finv = nullptr;  // the plain forward keeps the rows in their order
   a.h = static_cast<const uint16_t*>(h);
   a.W = static_cast<const uint16_t*>(W);
   a.labels = labels;
-  a.L = L;
-  a.H = H;
-  a.V = V;
+  a.L = p.L;
+  a.H = p.H;
+  a.V = p.V;
   a.ignore_index = ignore_index;
   a.chunk_rows = p.chunk_rows;
   a.tile_rows = p.tile_rows;
@@ -196,11 +195,87 @@ extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int
   a.vtiles_per_seg = p.vtiles_per_seg;
   a.xcd_map = p.xcd_map;
   a.hdr = hdr;
-  a.part_m = at<float>(workspace, p.off_pm);
-  a.part_s = at<float>(workspace, p.off_ps);
-  a.block_sum = at<float>(workspace, p.off_bsum);
+  a.part_m = at<float>(base, p.off_pm);
+  a.part_s = at<float>(base, p.off_ps);
+  a.block_sum = at<float>(base, p.off_bsum);
   if (launch_fwd(a, loss_out, lse_out, s) != hipSuccess) return LMCE_ERR_HIP;
   return LMCE_OK;
+}
+
+}  // namespace
+}  // namespace lmce
+
+extern "C" int lmce_fwd(const void* h, const void* W, const int64_t* labels, int64_t L, int64_t H, int64_t V,
+                        int64_t ignore_index, int64_t chunk_rows, float* loss_out, float* lse_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(L, H, V, chunk_rows, &p);
+  if (st != LMCE_OK) return st;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(labels, 8) || !aligned(loss_out, 4) || !aligned(lse_out, 4) ||
+      !aligned(workspace, 256))
+    return LMCE_ERR_NULL;
+  if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
+  return fwd_launch(p, h, W, labels, ignore_index, loss_out, lse_out, workspace, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------ no-allocation forward
+// lmce_fwd_noalloc runs the plain forward's kernels on a fixed area of device
+// memory that the library itself holds, `scratch`, instead of a workspace
+// the caller allocates.  The area has room for the forward's part of the
+// workspace layout (header, per-row partials of the vocabulary segments,
+// block sums: about 64 bytes per row), which covers L up to 2^20 rows.  Each
+// device the library runs on holds its own copy until the process ends.
+namespace lmce {
+namespace {
+
+constexpr size_t kScratchBytes = size_t(65) << 20;
+constexpr int64_t kScratchMaxRows = int64_t(1) << 20;  // the forward layout of 2^20 rows (8 segments) needs 64.06 MiB
+constexpr int kMaxScratchDevices = 64;
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (in host code the array's name is only a host-side stand-in).
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LMCE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return LMCE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return LMCE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LMCE_OK;
+}
+
+}  // namespace
+}  // namespace lmce
+
+extern "C" int lmce_fwd_noalloc(const void* h, const void* W, const int64_t* labels, int64_t L, int64_t H,
+                                int64_t V, int64_t ignore_index, int64_t chunk_rows, float* loss_out, float* lse_out,
+                                void* stream) {
+  Plan p;
+  int st = make_plan(L, H, V, chunk_rows, &p);
+  if (st != LMCE_OK) return st;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(labels, 8) || !aligned(loss_out, 4) || !aligned(lse_out, 4))
+    return LMCE_ERR_NULL;
+  if (L > kScratchMaxRows || p.off_hT > kScratchBytes) return LMCE_ERR_SCRATCH;  // the forward's part of the layout
+  void* base = nullptr;
+  st = scratch_on_current_device(&base);
+  if (st != LMCE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The area keeps the previous call's contents: clear the header (with a
+  // fill kernel, which graph capture records as an ordinary node), so that
+  // this call's status starts empty; every other part is written before it
+  // is read.
+  if (launch_zero_u32(static_cast<unsigned*>(base), (int)(sizeof(WsHeader) / sizeof(unsigned)), s) != hipSuccess)
+    return LMCE_ERR_HIP;
+  return fwd_launch(p, h, W, labels, ignore_index, loss_out, lse_out, base, s);
 }
 
 namespace {

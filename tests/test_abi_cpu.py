@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_strerror(lib):
     assert lib.lmce_version() >= 100
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert len(_lib.strerror(code)) > 0
     assert _lib.strerror(12345) == "unknown status"
 
@@ -172,3 +172,16 @@ def test_golden_facts_cite_the_pages():
             continue
         assert key in facts["_cite"], f"{key} has no citation"
     assert math.isclose(facts["card_memory_gb"], 80)
+
+
+def test_noalloc_forward_rejects_before_enqueuing(lib):
+    """lmce_fwd_noalloc: shape and pointer errors as lmce_fwd, and shapes past
+    its fixed area (L > 2^20 rows) are refused before any device call."""
+    f = lib.lmce_fwd_noalloc
+    assert f(FAKE, FAKE, FAKE, 0, 256, 4096, -100, 256, FAKE, FAKE, None) == _lib.LMCE_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 512, 100, 4096, -100, 256, FAKE, FAKE, None) == _lib.LMCE_ERR_UNSUPPORTED
+    assert f(None, FAKE, FAKE, 512, 256, 4096, -100, 256, FAKE, FAKE, None) == _lib.LMCE_ERR_NULL
+    assert f(FAKE + 2, FAKE, FAKE, 512, 256, 4096, -100, 256, FAKE, FAKE, None) == _lib.LMCE_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 512, 256, 4096, -100, 256, FAKE, None, None) == _lib.LMCE_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, (1 << 20) + 1, 256, 151936, -100, 256, FAKE, FAKE, None) == _lib.LMCE_ERR_SCRATCH
+    assert f(FAKE, FAKE, FAKE, 1 << 21, 128, 1, -100, 256, FAKE, FAKE, None) == _lib.LMCE_ERR_SCRATCH
