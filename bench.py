@@ -137,8 +137,10 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="rows of the CPU-baseline sample (about 10-30 s of oracle work at the default workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pair", choices=["train", "plain"], default="train",
-                    help="train: lmce_fwd_train + lmce_bwd_train; plain: lmce_fwd + lmce_bwd_dh + lmce_bwd_dW")
+    ap.add_argument("--pair", choices=["train", "plain", "chunked"], default="train",
+                    help="train: lmce_fwd_train + lmce_bwd_train; plain: lmce_fwd + lmce_bwd_dh + lmce_bwd_dW; "
+                         "chunked: the pages' own formulation, lmce_chunked_fwd + lmce_chunked_bwd (each chunk's "
+                         "logits materialised)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (scale for HBM byte counters) and exit")
     args = ap.parse_args()
@@ -175,7 +177,8 @@ def main():
     h, W, y = synth.make(wl, device=dev)
     n_valid = int((y != -100).sum())
     L, H, V = wl.L, wl.H, wl.V
-    ws_bytes = lm.lmce_workspace_size(L, H, V, chunk)
+    chunked = args.pair == "chunked"
+    ws_bytes = lm.lmce_chunked_workspace_size(L, H, V, chunk) if chunked else lm.lmce_workspace_size(L, H, V, chunk)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     lse = torch.empty(L, dtype=torch.float32, device=dev)
@@ -191,32 +194,29 @@ def main():
     # (name, kernel that dominates the call, algorithmic flops) per call of a step
     f_fwd = 2.0 * L * H * V
     f_nhv = 1.0 * n_valid * H * V
+    # (name, kernel that dominates the call, algorithmic flops, the call) per call of a step
     if plain:
-        calls = [("lmce_fwd", "k_fwd", f_fwd), ("lmce_bwd_dh", "k_bwd_dh", 3 * f_nhv),
-                 ("lmce_bwd_dW", "k_bwd_dW", 3 * f_nhv)]
+        calls = [("lmce_fwd", "k_fwd", f_fwd, lambda: lm.lmce_fwd(h, W, y, -100, chunk, ws, loss, lse)),
+                 ("lmce_bwd_dh", "k_bwd_dh", 3 * f_nhv, lambda: lm.lmce_bwd_dh(h, W, y, lse, g, -100, chunk, ws, dh)),
+                 ("lmce_bwd_dW", "k_bwd_dW", 3 * f_nhv, lambda: lm.lmce_bwd_dW(h, W, y, lse, g, -100, chunk, ws, dW))]
+    elif chunked:
+        calls = [("lmce_chunked_fwd", "k_gemm", f_fwd,
+                  lambda: lm.lmce_chunked_fwd(h, W, y, -100, chunk, ws, loss, lse)),
+                 ("lmce_chunked_bwd", "k_gemm", 6 * f_nhv,
+                  lambda: lm.lmce_chunked_bwd(h, W, y, g, -100, chunk, ws, dh, dW))]
     else:
-        calls = [("lmce_fwd_train", "k_fwd_dh", f_fwd + 2 * f_nhv), ("lmce_bwd_train", "k_bwd_dW", 4 * f_nhv)]
+        calls = [("lmce_fwd_train", "k_fwd_dh", f_fwd + 2 * f_nhv,
+                  lambda: lm.lmce_fwd_train(h, W, y, -100, chunk, ws, loss, lse)),
+                 ("lmce_bwd_train", "k_bwd_dW", 4 * f_nhv,
+                  lambda: lm.lmce_bwd_train(h, W, y, lse, g, -100, chunk, ws, dh, dW))]
 
     def step(ev=None):
+        for c, call in enumerate(calls):
+            if ev is not None:
+                ev[c].record(stream)
+            call[3]()
         if ev is not None:
-            ev[0].record(stream)
-        if plain:
-            lm.lmce_fwd(h, W, y, -100, chunk, ws, loss, lse)
-            if ev is not None:
-                ev[1].record(stream)
-            lm.lmce_bwd_dh(h, W, y, lse, g, -100, chunk, ws, dh)
-            if ev is not None:
-                ev[2].record(stream)
-            lm.lmce_bwd_dW(h, W, y, lse, g, -100, chunk, ws, dW)
-            if ev is not None:
-                ev[3].record(stream)
-        else:
-            lm.lmce_fwd_train(h, W, y, -100, chunk, ws, loss, lse)
-            if ev is not None:
-                ev[1].record(stream)
-            lm.lmce_bwd_train(h, W, y, lse, g, -100, chunk, ws, dh, dW)
-            if ev is not None:
-                ev[2].record(stream)
+            ev[len(calls)].record(stream)
 
     for i in range(args.warmup):
         step()
@@ -241,7 +241,7 @@ def main():
     f_alg = f_fwd + 6 * f_nhv
     tflops = f_alg / (ms_step / 1000.0) / 1e12
     dom = max(range(len(calls)), key=lambda c: call_ms[c])
-    dom_name, dom_kernel, dom_flops = calls[dom]
+    dom_name, dom_kernel, dom_flops = calls[dom][:3]
     dom_tflops = dom_flops / (call_ms[dom] / 1000.0) / 1e12
 
     result = {

@@ -186,6 +186,36 @@ int lmce_bwd_train(const void* h, const void* W, const int64_t* labels, const fl
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The pages' own chunked formulation, as a comparison path (TRL docs
+ * "Training Beyond 1M Tokens", section "The massive logits matrix: chunk
+ * it": a few hundred rows at a time, 256 in TRL, each chunk's logits formed,
+ * its loss taken and the pieces summed; the backward walks the chunks again,
+ * each adding its share of dW).  Same definition and results (within
+ * rounding) as lmce_fwd / lmce_bwd, but each chunk's logits ARE written to
+ * the workspace as fp32 [chunk_rows][V] (148 MiB at 256 x 151936) and read
+ * back, and dW is accumulated in memory once per chunk.
+ *
+ *   lmce_chunked_workspace_size: bytes for this shape: the chunk's logits,
+ *     its bf16 G and G^T, a K-tiled copy of W^T, dh partials of the chunk,
+ *     per-row nll (O(L) floats).
+ *   lmce_chunked_fwd: loss_out and lse_out as lmce_fwd.
+ *   lmce_chunked_bwd: dh_out and dW_out as lmce_bwd (overwritten); it
+ *     recomputes every chunk's logits and their lse, as autograd over a
+ *     checkpointed chunk would, so it takes no lse argument.
+ * chunk_rows is 1 .. 4096 (any value); H % 128 == 0; other limits, pointer
+ * rules, status reporting (lmce_read_status on this workspace) as above.
+ */
+int lmce_chunked_workspace_size(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, size_t* bytes);
+int lmce_chunked_fwd(const void* h, const void* W, const int64_t* labels,
+                     int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
+                     float* loss_out, float* lse_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+int lmce_chunked_bwd(const void* h, const void* W, const int64_t* labels,
+                     int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
+                     const float* grad_loss, float* dh_out, float* dW_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Synchronises `stream` and returns the asynchronous status recorded in the
  * workspace by every call on it since the previous lmce_read_status (the
  * flags of the calls accumulate; a later call never erases an earlier

@@ -30,6 +30,9 @@ __all__ = [
     "lmce_bwd_train",
     "lmce_read_status",
     "lmce_fwd_noalloc",
+    "lmce_chunked_workspace_size",
+    "lmce_chunked_fwd",
+    "lmce_chunked_bwd",
     "chunked_nll",
     "LmceError",
     "IGNORE_INDEX",
@@ -188,6 +191,52 @@ def lmce_bwd_dW(h, W, labels, lse, grad_loss=None, ignore_index=IGNORE_INDEX, ch
                 workspace=None, dW_out=None):
     """dW (fp32 [V, H]) alone."""
     return _bwd_one("dW", h, W, labels, lse, grad_loss, ignore_index, chunk_rows, workspace, dW_out)
+
+
+def lmce_chunked_workspace_size(L, H, V, chunk_rows=DEFAULT_CHUNK_ROWS) -> int:
+    """Workspace bytes of the materialised-chunk comparison path (one chunk's fp32 logits and more)."""
+    return _lib.chunked_workspace_size(L, H, V, chunk_rows)
+
+
+def _chunked_ws(L, H, V, chunk_rows, device, workspace):
+    need = _lib.chunked_workspace_size(L, H, V, chunk_rows)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, needs {need}")
+    return workspace
+
+
+def lmce_chunked_fwd(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS, workspace=None,
+                     loss_out=None, lse_out=None):
+    """The pages' chunked formulation: each chunk's logits materialised, loss and lse as lmce_fwd."""
+    L, H, V = _check_inputs(h, W, labels)
+    dev = h.device
+    ws = _chunked_ws(L, H, V, chunk_rows, dev, workspace)
+    loss = torch.empty((), dtype=torch.float32, device=dev) if loss_out is None else loss_out
+    lse = torch.empty(L, dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    st = _lib.chunked_fwd(h.data_ptr(), W.data_ptr(), labels.data_ptr(), L, H, V, ignore_index, chunk_rows,
+                          loss.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(st, "lmce_chunked_fwd")
+    return loss, lse
+
+
+def lmce_chunked_bwd(h, W, labels, grad_loss=None, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS,
+                     workspace=None, dh_out=None, dW_out=None):
+    """The pages' chunked formulation of the backward: dh and dW as lmce_bwd."""
+    L, H, V = _check_inputs(h, W, labels)
+    dev = h.device
+    if grad_loss is None:
+        grad_loss = torch.ones((), dtype=torch.float32, device=dev)
+    grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
+    ws = _chunked_ws(L, H, V, chunk_rows, dev, workspace)
+    dh = torch.empty(L, H, dtype=torch.float32, device=dev) if dh_out is None else dh_out
+    dW = torch.empty(V, H, dtype=torch.float32, device=dev) if dW_out is None else dW_out
+    st = _lib.chunked_bwd(h.data_ptr(), W.data_ptr(), labels.data_ptr(), L, H, V, ignore_index, chunk_rows,
+                          grad_loss.data_ptr(), dh.data_ptr(), dW.data_ptr(), ws.data_ptr(),
+                          ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(st, "lmce_chunked_bwd")
+    return dh, dW
 
 
 def lmce_read_status(workspace) -> int:

@@ -43,6 +43,11 @@ SIGNATURES = {
     "lmce_bwd_train": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                       _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_read_status": (ctypes.c_int, [_c_vp, _c_vp]),
+    "lmce_chunked_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(ctypes.c_size_t)]),
+    "lmce_chunked_fwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                        _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "lmce_chunked_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                        _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_fwd_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                         _c_vp, _c_vp, _c_vp]),
 }
@@ -126,6 +131,25 @@ def bwd_train(h_ptr, W_ptr, labels_ptr, lse_ptr, L, H, V, ignore_index, chunk_ro
 def fwd_noalloc(h_ptr, W_ptr, labels_ptr, L, H, V, ignore_index, chunk_rows, loss_ptr, lse_ptr, stream):
     return load().lmce_fwd_noalloc(h_ptr, W_ptr, labels_ptr, int(L), int(H), int(V), int(ignore_index),
                                    int(chunk_rows), loss_ptr, lse_ptr, stream)
+
+
+def chunked_workspace_size(L, H, V, chunk_rows) -> int:
+    n = ctypes.c_size_t(0)
+    check(load().lmce_chunked_workspace_size(int(L), int(H), int(V), int(chunk_rows), ctypes.byref(n)),
+          "lmce_chunked_workspace_size")
+    return int(n.value)
+
+
+def chunked_fwd(h_ptr, W_ptr, labels_ptr, L, H, V, ignore_index, chunk_rows, loss_ptr, lse_ptr, ws_ptr, ws_bytes,
+                stream):
+    return load().lmce_chunked_fwd(h_ptr, W_ptr, labels_ptr, int(L), int(H), int(V), int(ignore_index),
+                                   int(chunk_rows), loss_ptr, lse_ptr, ws_ptr, int(ws_bytes), stream)
+
+
+def chunked_bwd(h_ptr, W_ptr, labels_ptr, L, H, V, ignore_index, chunk_rows, grad_ptr, dh_ptr, dW_ptr, ws_ptr,
+                ws_bytes, stream):
+    return load().lmce_chunked_bwd(h_ptr, W_ptr, labels_ptr, int(L), int(H), int(V), int(ignore_index),
+                                   int(chunk_rows), grad_ptr, dh_ptr, dW_ptr, ws_ptr, int(ws_bytes), stream)
 
 
 def read_status(ws_ptr, stream) -> int:

@@ -99,6 +99,50 @@ struct BwdArgs {
   float* dW;
 };
 
+// ------------------------------------------------------------------ GEMM
+// C = alpha * A B^T on the tile engine: A has M rows, B has N rows, both bf16
+// with K contiguous, either linear (row r, K index k at r * ld + 2k bytes) or
+// K-tiled as the transposer writes them ((k / 128) * tstride + r * ld +
+// 2 (k % 128)).  256 x 256 output tiles; grid.y splits K into ksplit pieces
+// of kchunk (a multiple of 64, of 128 for a K-tiled operand), piece z writing
+// at C + z * c_split (elements).  Rows past M or N read as zero and are not
+// written; K past an operand's end reads as zero.
+enum GemmEpi {
+  kEpiStoreF32 = 0,   // C fp32 [M][ldc] = alpha * acc
+  kEpiAccF32 = 1,     // C fp32 [M][ldc] += alpha * acc
+  kEpiStoreBf16 = 2,  // C bf16 [M][ldc] = alpha * acc
+  kEpiSwigluFwd = 3,  // acc = gate/up pairs (32-column blocks interleaved): C bf16 [M][ldc] = silu(g) * u at column i
+  kEpiSwigluBwd = 4,  // acc = d(act) [M][N]: reads gate/up gu bf16 [M][2N] (interleaved); C bf16 [M][2N] = d(gate/up)
+                      // interleaved, aux bf16 [M][N] = silu(g) * u
+  kEpiAccF32Gu = 5,   // C (gate rows) and C2 (up rows) fp32 [M/2][ldc] += alpha * acc, A rows interleaved
+};
+
+struct GemmArgs {
+  const void* A;
+  uint64_t a_bytes;     // bytes readable from A
+  uint32_t a_ld, a_tstride;
+  int a_tiled;
+  const void* B;
+  uint64_t b_bytes;
+  uint32_t b_ld, b_tstride;
+  int b_tiled;
+  int64_t M, N;
+  int64_t kchunk;       // K of one split piece
+  int ksplit;
+  int epi;
+  float alpha;
+  void* C;
+  void* C2;
+  int64_t ldc, c_split;
+  const uint16_t* gu;   // kEpiSwigluBwd: gate/up values
+  uint16_t* aux;        // kEpiSwigluBwd: act output
+  int64_t ld_aux;
+  int patch_m;          // tile order: patches of patch_m (1, 2, 4, 8) x (32 / patch_m) tiles, one patch per XCD
+                        // at a time; 0: row-major
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
 hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int64_t ignore_index, WsHeader* hdr,
                                int saved, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
