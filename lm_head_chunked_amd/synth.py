@@ -26,6 +26,15 @@ Recipe (fixed, so that every run draws the same bits for a given seed):
 
 Draws on a CUDA device and on the CPU give different bits for the same seed;
 a test that compares the two paths draws once and copies the tensors.
+
+The MLP block of the same page's section "One GPU is not enough: split the
+sequence across many" (down_proj(act_fn(gate_proj(x)) * up_proj(x)), an MLP
+that widens each token from 2560 to 9728 in the Qwen3-4B model) gets its own
+workloads: x = N(0, 1) (a normalised hidden state), the three weights
+N(0, 0.02^2), the upstream gradient dy = N(0, 1), all rounded to bf16, each
+from its own generator seeded with ``seed * 7919 + k`` (k = 10 x, 11 Wg,
+12 Wu, 13 Wd, 14 dy).  The long one has 262,144 rows: one GPU's share of a
+1,048,576-token sequence split over four GPUs, the page's own example.
 """
 
 from __future__ import annotations
@@ -151,3 +160,49 @@ def shift_labels(tokens: torch.Tensor, ignore_index: int = IGNORE_INDEX) -> torc
         y[:-1] = tokens[1:]
         y[-1] = ignore_index
     return y
+
+
+@dataclass(frozen=True)
+class MlpWorkload:
+    name: str
+    L: int
+    H: int
+    I: int
+    x_scale: float
+    w_std: float
+    dy_scale: float
+    chunk_rows: int
+
+    def with_rows(self, L: int) -> "MlpWorkload":
+        return replace(self, L=L)
+
+
+MLP_WORKLOADS = {
+    # small case the fp64 oracle finishes in well under a second
+    "mlp_tiny": MlpWorkload("mlp_tiny", 512, 256, 768, 1.0, 0.02, 1.0, 256),
+    # Qwen3-4B MLP (2560 -> 9728), one GPU's 262,144-row share of 1,048,576 tokens over 4 GPUs
+    "qwen3_4b_mlp_256k": MlpWorkload("qwen3_4b_mlp_256k", 262144, 2560, 9728, 1.0, 0.02, 1.0, 16384),
+}
+
+
+def _draw_bf16(shape, scale, device, seed, k):
+    t = torch.randn(*shape, generator=_gen(device, seed, k), device=device, dtype=torch.float32)
+    if scale != 1.0:
+        t.mul_(scale)
+    return t.to(torch.bfloat16)
+
+
+def make_mlp(wl, device="cpu", seed: int = 0):
+    """(x [L,H], Wg [I,H], Wu [I,H], Wd [H,I], dy [L,H]), all bf16, for an MLP workload or its name."""
+    if isinstance(wl, str):
+        wl = MLP_WORKLOADS[wl]
+    return (_draw_bf16((wl.L, wl.H), wl.x_scale, device, seed, 10),
+            _draw_bf16((wl.I, wl.H), wl.w_std, device, seed, 11),
+            _draw_bf16((wl.I, wl.H), wl.w_std, device, seed, 12),
+            _draw_bf16((wl.H, wl.I), wl.w_std, device, seed, 13),
+            _draw_bf16((wl.L, wl.H), wl.dy_scale, device, seed, 14))
+
+
+def random_mlp_case(L, H, I, seed=0, w_std=0.02, device="cpu"):
+    """A small ad-hoc MLP case (for property and edge tests)."""
+    return make_mlp(MlpWorkload("adhoc", L, H, I, 1.0, w_std, 1.0, 256), device, seed)

@@ -45,3 +45,15 @@ def test_zipf_labels_follow_the_law():
 def test_shift_labels():
     t = torch.tensor([5, 6, 7, 8])
     assert synth.shift_labels(t).tolist() == [6, 7, 8, -100]
+
+
+def test_mlp_draws_are_seeded_and_shaped():
+    x, Wg, Wu, Wd, dy = synth.make_mlp("mlp_tiny")
+    wl = synth.MLP_WORKLOADS["mlp_tiny"]
+    assert x.shape == (wl.L, wl.H) and Wg.shape == (wl.I, wl.H) and Wu.shape == (wl.I, wl.H)
+    assert Wd.shape == (wl.H, wl.I) and dy.shape == (wl.L, wl.H)
+    assert all(t.dtype == torch.bfloat16 for t in (x, Wg, Wu, Wd, dy))
+    x2 = synth.make_mlp("mlp_tiny")[0]
+    assert torch.equal(x, x2)
+    assert not torch.equal(Wg, Wu)  # separate generators
+    assert abs(float(Wg.float().std()) - 0.02) < 0.002 and abs(float(x.float().std()) - 1.0) < 0.05
