@@ -127,6 +127,95 @@ def cpu_baseline(wl, W_cpu, h_rows, y_rows, n_valid):
     return info, ref
 
 
+def bench_mlp(args):
+    """The sequence-tiled MLP block: one step = lmce_mlp_fwd + lmce_mlp_bwd over the workload.
+
+    Algorithmic flops per step (H hidden, I intermediate, L rows):
+      forward   6 L H I    (gate and up projections 4 L H I, down projection 2 L H I)
+      backward 16 L H I    (the gate/up recompute the tiling needs 4 L H I, d(act) 2 L H I,
+                            dx 4 L H I, dWd 2 L H I, dWg and dWu 4 L H I)
+    """
+    import torch
+
+    import lm_head_chunked_amd as lm
+    from lm_head_chunked_amd import synth
+
+    name = args.workload if args.workload in synth.MLP_WORKLOADS else "qwen3_4b_mlp_256k"
+    wl = synth.MLP_WORKLOADS[name]
+    chunk = args.chunk_rows or wl.chunk_rows
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, H, I = wl.L, wl.H, wl.I
+    log(f"[bench] mlp workload {wl.name} L={L} H={H} I={I} chunk_rows={chunk}")
+    x, Wg, Wu, Wd, dy = synth.make_mlp(wl, device=dev)
+    ws_bytes = lm.lmce_mlp_workspace_size(L, H, I, chunk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    y, dx = torch.empty(L, H, **f32), torch.empty(L, H, **f32)
+    dWg, dWu, dWd = torch.empty(I, H, **f32), torch.empty(I, H, **f32), torch.empty(H, I, **f32)
+    stream = torch.cuda.current_stream(dev)
+    lhi = float(L) * H * I
+    calls = [("lmce_mlp_fwd", 6 * lhi, lambda: lm.lmce_mlp_fwd(x, Wg, Wu, Wd, chunk, ws, y)),
+             ("lmce_mlp_bwd", 16 * lhi, lambda: lm.lmce_mlp_bwd(x, Wg, Wu, Wd, dy, chunk, ws, dx, dWg, dWu, dWd))]
+    for i in range(args.warmup):
+        for c in calls:
+            c[2]()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for c, call in enumerate(calls):
+            events[i][c].record(stream)
+            call[2]()
+        events[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [statistics.mean(e[c].elapsed_time(e[c + 1]) for e in events) for c in range(2)]
+    ms_step = wall * 1000.0 / args.steps
+    tflops = 22 * lhi / (ms_step / 1000.0) / 1e12
+    log(f"[bench] {args.steps} steps: {ms_step:.1f} ms/step; fwd {call_ms[0]:.1f} ms, bwd {call_ms[1]:.1f} ms; "
+        f"{tflops:.0f} TFLOP/s")
+    dom = max(range(2), key=lambda c: call_ms[c])
+    dom_tflops = calls[dom][1] / (call_ms[dom] / 1000.0) / 1e12
+    untiled = 4 * L * I * 2
+    result = {
+        "metric": "sequence-tiled MLP block fwd+bwd tokens/s and % bf16 MFMA peak (Qwen3-4B MLP)",
+        "value": L * args.steps / wall, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "L": L, "H": H, "I": I, "chunk_rows": chunk, "achieved_tflops": tflops,
+                   "peak_frac_bf16": tflops / PEAK_BF16_TFLOPS, "flops_per_step": 22 * lhi,
+                   "call_ms": {c[0]: t for c, t in zip(calls, call_ms)}, "workspace_bytes": ws_bytes,
+                   "untiled_intermediates_bytes": untiled, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm", "call": calls[dom][0], "achieved": dom_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None, "mean_ms": call_ms[dom]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+
+        import oracle
+
+        threads, nproc, model = host_cores()
+        n = min(args.cpu_rows, L)
+        xs, dys = x[:n].float().cpu().numpy(), dy[:n].float().cpu().numpy()
+        Ws = [t.float().cpu().numpy() for t in (Wg, Wu, Wd)]
+        with threadpoolctl.threadpool_limits(limits=threads, user_api="blas"):
+            t1 = time.perf_counter()
+            oracle.mlp_fwd_bwd(xs, *Ws, dys)
+            dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                  "nproc": nproc, "cpu_model": model,
+                                  "sample": f"first {n} rows of {wl.name}: fp64 forward+backward in {dt:.2f} s"}
+    print(json.dumps(result), flush=True)
+    del x, Wg, Wu, Wd, dy, y, dx, dWg, dWu, dWd, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +230,9 @@ def main():
                     help="train: lmce_fwd_train + lmce_bwd_train; plain: lmce_fwd + lmce_bwd_dh + lmce_bwd_dW; "
                          "chunked: the pages' own formulation, lmce_chunked_fwd + lmce_chunked_bwd (each chunk's "
                          "logits materialised)")
+    ap.add_argument("--op", choices=["loss", "mlp"], default="loss",
+                    help="loss: the LM-head + cross-entropy loss (default); mlp: the sequence-tiled MLP block "
+                         "(lmce_mlp_fwd + lmce_mlp_bwd) on --workload qwen3_4b_mlp_256k unless given")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (scale for HBM byte counters) and exit")
     args = ap.parse_args()
@@ -168,6 +260,8 @@ def main():
         return
 
     _lib.load()
+    if args.op == "mlp":
+        return bench_mlp(args)
     wl = synth.WORKLOADS[args.workload]
     chunk = args.chunk_rows or wl.chunk_rows
     dev = torch.device("cuda:0")

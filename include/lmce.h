@@ -216,6 +216,39 @@ int lmce_chunked_bwd(const void* h, const void* W, const int64_t* labels,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Sequence-tiled MLP block (TRL docs "Training Beyond 1M Tokens", section
+ * "One GPU is not enough: split the sequence across many": the line
+ * down_proj(act_fn(gate_proj(x)) * up_proj(x)) builds four tensors at the
+ * full intermediate width; TRL PR #6845 lists MLP sequence tiling as the
+ * lever that removes them).  act_fn = SiLU.  The rows are processed
+ * chunk_rows at a time, so those four intermediates exist (in bf16) for one
+ * chunk only:
+ *   y   = (silu(x Wg^T) * (x Wu^T)) Wd^T
+ *   dx, dWg, dWu, dWd: the gradients for an upstream dy of y.
+ *
+ *   x   bf16 [L, H]   Wg, Wu  bf16 [I, H] (gate_proj, up_proj weights)
+ *   Wd  bf16 [H, I]   (down_proj weight)     dy  bf16 [L, H]
+ *   y_out, dx_out fp32 [L, H]; dWg_out, dWu_out fp32 [I, H]; dWd_out fp32
+ *   [H, I]; every output overwritten.
+ * The backward recomputes each chunk's gate and up projections (the forward
+ * keeps nothing of them) and takes no forward state: it may run on its own.
+ * Limits: 128 <= H <= 16384 with H % 128 == 0, 64 <= I <= 65536 with
+ * I % 64 == 0, 1 <= L <= 2^24, 1 <= chunk_rows <= 65536, and 4 I H and
+ * 4 I ceil(chunk_rows / 128) 128 at most 2^31 - 4096 (LMCE_ERR_UNSUPPORTED
+ * otherwise).  The workspace holds the packed weights and their transposes
+ * (5 I H bf16) and one chunk's intermediates; lmce_mlp_workspace_size gives
+ * its size.  Pointer rules as above; there is no asynchronous status.
+ */
+int lmce_mlp_workspace_size(int64_t L, int64_t H, int64_t I, int64_t chunk_rows, size_t* bytes);
+int lmce_mlp_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                 int64_t L, int64_t H, int64_t I, int64_t chunk_rows, float* y_out,
+                 void* workspace, size_t workspace_bytes, void* stream);
+int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd, const void* dy,
+                 int64_t L, int64_t H, int64_t I, int64_t chunk_rows,
+                 float* dx_out, float* dWg_out, float* dWu_out, float* dWd_out,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Synchronises `stream` and returns the asynchronous status recorded in the
  * workspace by every call on it since the previous lmce_read_status (the
  * flags of the calls accumulate; a later call never erases an earlier

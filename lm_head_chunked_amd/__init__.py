@@ -33,6 +33,9 @@ __all__ = [
     "lmce_chunked_workspace_size",
     "lmce_chunked_fwd",
     "lmce_chunked_bwd",
+    "lmce_mlp_workspace_size",
+    "lmce_mlp_fwd",
+    "lmce_mlp_bwd",
     "chunked_nll",
     "LmceError",
     "IGNORE_INDEX",
@@ -237,6 +240,62 @@ def lmce_chunked_bwd(h, W, labels, grad_loss=None, ignore_index=IGNORE_INDEX, ch
                           ws.numel() * ws.element_size(), _stream(dev))
     _lib.check(st, "lmce_chunked_bwd")
     return dh, dW
+
+
+def _check_mlp(x, Wg, Wu, Wd, dy=None):
+    ts = [x, Wg, Wu, Wd] + ([dy] if dy is not None else [])
+    if not all(t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous() and t.dim() == 2 for t in ts):
+        raise TypeError("x, Wg, Wu, Wd (and dy) must be contiguous 2-D bf16 device tensors")
+    L, H = x.shape
+    I = Wg.shape[0]
+    if Wg.shape != (I, H) or Wu.shape != (I, H) or Wd.shape != (H, I) or (dy is not None and dy.shape != (L, H)):
+        raise ValueError(f"shapes: x {tuple(x.shape)}, Wg {tuple(Wg.shape)}, Wu {tuple(Wu.shape)}, "
+                         f"Wd {tuple(Wd.shape)}" + ("" if dy is None else f", dy {tuple(dy.shape)}"))
+    return L, H, I
+
+
+def lmce_mlp_workspace_size(L, H, I, chunk_rows) -> int:
+    """Workspace bytes of the sequence-tiled MLP (packed weights and one chunk's intermediates)."""
+    return _lib.mlp_workspace_size(L, H, I, chunk_rows)
+
+
+def _mlp_ws(L, H, I, chunk_rows, device, workspace):
+    need = _lib.mlp_workspace_size(L, H, I, chunk_rows)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, needs {need}")
+    return workspace
+
+
+def lmce_mlp_fwd(x, Wg, Wu, Wd, chunk_rows=4096, workspace=None, y_out=None):
+    """y = down_proj(silu(gate_proj(x)) * up_proj(x)) (fp32 [L, H]), chunk_rows rows at a time."""
+    L, H, I = _check_mlp(x, Wg, Wu, Wd)
+    dev = x.device
+    ws = _mlp_ws(L, H, I, chunk_rows, dev, workspace)
+    y = torch.empty(L, H, dtype=torch.float32, device=dev) if y_out is None else y_out
+    st = _lib.mlp_fwd(x.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), Wd.data_ptr(), L, H, I, chunk_rows, y.data_ptr(),
+                      ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(st, "lmce_mlp_fwd")
+    return y
+
+
+def lmce_mlp_bwd(x, Wg, Wu, Wd, dy, chunk_rows=4096, workspace=None, dx_out=None, dWg_out=None, dWu_out=None,
+                 dWd_out=None):
+    """(dx, dWg, dWu, dWd), fp32, for the upstream gradient dy (bf16 [L, H]) of y."""
+    L, H, I = _check_mlp(x, Wg, Wu, Wd, dy)
+    dev = x.device
+    ws = _mlp_ws(L, H, I, chunk_rows, dev, workspace)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dx = torch.empty(L, H, **f32) if dx_out is None else dx_out
+    dWg = torch.empty(I, H, **f32) if dWg_out is None else dWg_out
+    dWu = torch.empty(I, H, **f32) if dWu_out is None else dWu_out
+    dWd = torch.empty(H, I, **f32) if dWd_out is None else dWd_out
+    st = _lib.mlp_bwd(x.data_ptr(), Wg.data_ptr(), Wu.data_ptr(), Wd.data_ptr(), dy.data_ptr(), L, H, I, chunk_rows,
+                      dx.data_ptr(), dWg.data_ptr(), dWu.data_ptr(), dWd.data_ptr(), ws.data_ptr(),
+                      ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(st, "lmce_mlp_bwd")
+    return dx, dWg, dWu, dWd
 
 
 def lmce_read_status(workspace) -> int:

@@ -48,6 +48,11 @@ SIGNATURES = {
                                         _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_chunked_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                         _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "lmce_mlp_workspace_size": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.POINTER(ctypes.c_size_t)]),
+    "lmce_mlp_fwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp,
+                                    _c_vp, ctypes.c_size_t, _c_vp]),
+    "lmce_mlp_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                    _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_fwd_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                         _c_vp, _c_vp, _c_vp]),
 }
@@ -150,6 +155,24 @@ def chunked_bwd(h_ptr, W_ptr, labels_ptr, L, H, V, ignore_index, chunk_rows, gra
                 ws_bytes, stream):
     return load().lmce_chunked_bwd(h_ptr, W_ptr, labels_ptr, int(L), int(H), int(V), int(ignore_index),
                                    int(chunk_rows), grad_ptr, dh_ptr, dW_ptr, ws_ptr, int(ws_bytes), stream)
+
+
+def mlp_workspace_size(L, H, I, chunk_rows) -> int:
+    n = ctypes.c_size_t(0)
+    check(load().lmce_mlp_workspace_size(int(L), int(H), int(I), int(chunk_rows), ctypes.byref(n)),
+          "lmce_mlp_workspace_size")
+    return int(n.value)
+
+
+def mlp_fwd(x_ptr, Wg_ptr, Wu_ptr, Wd_ptr, L, H, I, chunk_rows, y_ptr, ws_ptr, ws_bytes, stream):
+    return load().lmce_mlp_fwd(x_ptr, Wg_ptr, Wu_ptr, Wd_ptr, int(L), int(H), int(I), int(chunk_rows), y_ptr, ws_ptr,
+                               int(ws_bytes), stream)
+
+
+def mlp_bwd(x_ptr, Wg_ptr, Wu_ptr, Wd_ptr, dy_ptr, L, H, I, chunk_rows, dx_ptr, dWg_ptr, dWu_ptr, dWd_ptr, ws_ptr,
+            ws_bytes, stream):
+    return load().lmce_mlp_bwd(x_ptr, Wg_ptr, Wu_ptr, Wd_ptr, dy_ptr, int(L), int(H), int(I), int(chunk_rows),
+                               dx_ptr, dWg_ptr, dWu_ptr, dWd_ptr, ws_ptr, int(ws_bytes), stream)
 
 
 def read_status(ws_ptr, stream) -> int:

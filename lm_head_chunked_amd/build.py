@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblmce.so"
-SOURCES = ["lmce_api.hip", "lmce_fwd.hip", "lmce_bwd.hip", "lmce_gemm.hip", "lmce_chunked.hip"]
+SOURCES = ["lmce_api.hip", "lmce_fwd.hip", "lmce_bwd.hip", "lmce_gemm.hip", "lmce_chunked.hip", "lmce_mlp.hip"]
 ARCH = "gfx950"
 
 

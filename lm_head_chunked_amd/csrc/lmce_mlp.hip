@@ -1,0 +1,310 @@
+// Sequence-tiled MLP block, forward and backward, on gfx950.
+//
+// Page: TRL docs "Training Beyond 1M Tokens", section "One GPU is not
+// enough: split the sequence across many": one line of the model,
+// down_proj(act_fn(gate_proj(x)) * up_proj(x)), builds four tensors at the
+// full intermediate width I (4 x 19 GB at a million tokens and I = 9728).
+// TRL PR #6845 lists MLP sequence tiling as the lever that removes them: the
+// rows are processed a block at a time, so those tensors exist only for
+// chunk_rows rows (in bf16, 2 bytes per element as on the page).  act_fn is
+// SiLU.
+//
+// Weights: Wg, Wu [I][H] (gate_proj, up_proj), Wd [H][I] (down_proj), bf16.
+// Per call the library packs Wg and Wu into one [2I][H] matrix whose rows
+// alternate 32-row blocks of the two (rows 64q + j = Wg row 32q + j, rows
+// 64q + 32 + j = Wu row 32q + j), so that one GEMM gives each lane the gate
+// and up values of the same units, and writes K-tiled transposes of the
+// packed matrix and of Wd for the backward's contractions over I and H.
+//
+// Forward, per chunk c:  p_c = silu(x_c Wg^T) * (x_c Wu^T)   (GEMM, fused epilogue, bf16)
+//                        y_c = p_c Wd^T                      (GEMM, fp32 out)
+// Backward, per chunk c (upstream dy):
+//   gu_c = x_c [Wg; Wu]^T            recomputed (GEMM, bf16)
+//   dp_c = dy_c Wd, and in the same epilogue dg_c, du_c (bf16) and p_c (bf16)
+//   dx_c = dg_c Wg + du_c Wu          (one GEMM over the packed 2I)
+//   dWd += dy_c^T p_c, dWg += dg_c^T x_c, dWu += du_c^T x_c   (GEMMs, K = the chunk's rows)
+
+#include "lmce_device.h"
+#include "lmce_internal.h"
+#include "lmce.h"
+
+namespace lmce {
+namespace {
+
+// Packed gate/up rows (one 2I row per workgroup).
+__global__ __launch_bounds__(256) void k_pack_gu(const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu,
+                                                 int64_t H, uint16_t* __restrict__ Wgu) {
+  const int64_t r = blockIdx.x;
+  const int64_t q = r >> 6, j = r & 63;
+  const uint16_t* src = (j < 32 ? Wg : Wu) + (q * 32 + (j & 31)) * H;
+  const uint4* in = reinterpret_cast<const uint4*>(src);
+  uint4* out = reinterpret_cast<uint4*>(Wgu + r * H);
+  for (int64_t c = threadIdx.x; c < H / 8; c += 256) out[c] = in[c];
+}
+
+struct MlpPlan {
+  int64_t L, H, I, cr, Rp;
+  size_t off_Wgu, off_WguT, off_WdT, off_gu, off_act, off_dgu, off_actT, off_dguT, off_dyT, off_xT, total;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int mlp_plan(int64_t L, int64_t H, int64_t I, int64_t chunk_rows, MlpPlan* p) {
+  if (L < 1 || L > (int64_t(1) << 24) || H < 128 || H > 16384 || I < 64 || I > 65536) return LMCE_ERR_SHAPE;
+  if (H % 128 != 0 || I % 64 != 0 || chunk_rows < 1 || chunk_rows > 65536) return LMCE_ERR_UNSUPPORTED;
+  p->L = L;
+  p->H = H;
+  p->I = I;
+  p->cr = chunk_rows < L ? chunk_rows : L;
+  p->Rp = (p->cr + 127) / 128 * 128;
+  // every K-tiled operand (the packed weights over K = 2I, the chunk's
+  // gate/up gradient over K = its rows) must fit one buffer resource, so
+  // that its 32-bit offsets stay exact
+  const int64_t kMaxRes = 0x7ffff000;
+  if (4 * I * H > kMaxRes || 4 * I * p->Rp > kMaxRes) return LMCE_ERR_UNSUPPORTED;
+  const size_t b = 2;  // bf16
+  size_t off = up256(sizeof(WsHeader));
+  p->off_Wgu = off;
+  off = up256(off + b * 2 * I * H);
+  p->off_WguT = off;
+  off = up256(off + b * 2 * I * H);
+  p->off_WdT = off;
+  off = up256(off + b * H * I);
+  p->off_gu = off;
+  off = up256(off + b * p->cr * 2 * I);
+  p->off_act = off;
+  off = up256(off + b * p->cr * I);
+  p->off_dgu = off;
+  off = up256(off + b * p->cr * 2 * I);
+  p->off_actT = off;
+  off = up256(off + b * p->Rp * I);
+  p->off_dguT = off;
+  off = up256(off + b * p->Rp * 2 * I);
+  p->off_dyT = off;
+  off = up256(off + b * p->Rp * H);
+  p->off_xT = off;
+  off = up256(off + b * p->Rp * H);
+  p->total = off;
+  return LMCE_OK;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return ptr != nullptr && (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// A linear operand: `rows` rows of ld_elems bf16 each.
+void set_a_linear(GemmArgs& g, const void* p, int64_t rows, int64_t ld_elems) {
+  g.A = p;
+  g.a_bytes = (uint64_t)rows * ld_elems * 2;
+  g.a_ld = (uint32_t)(ld_elems * 2);
+  g.a_tiled = 0;
+}
+void set_b_linear(GemmArgs& g, const void* p, int64_t rows, int64_t ld_elems) {
+  g.B = p;
+  g.b_bytes = (uint64_t)rows * ld_elems * 2;
+  g.b_ld = (uint32_t)(ld_elems * 2);
+  g.b_tiled = 0;
+}
+// A K-tiled operand as the transposer writes it: `rows` rows, K padded to kpad.
+void set_a_tiled(GemmArgs& g, const void* p, int64_t rows, int64_t kpad) {
+  g.A = p;
+  g.a_bytes = (uint64_t)rows * kpad * 2;
+  g.a_ld = 256;
+  g.a_tstride = (uint32_t)(rows * 256);
+  g.a_tiled = 1;
+}
+void set_b_tiled(GemmArgs& g, const void* p, int64_t rows, int64_t kpad) {
+  g.B = p;
+  g.b_bytes = (uint64_t)rows * kpad * 2;
+  g.b_ld = 256;
+  g.b_tstride = (uint32_t)(rows * 256);
+  g.b_tiled = 1;
+}
+
+// p_c = silu(g) * u of rows [r0, r0 + rows) into the act area; with
+// store_gu, the bf16 gate/up values themselves into the gu area instead.
+hipError_t gate_up(const MlpPlan& p, const void* x, const uint16_t* Wgu, int64_t r0, int64_t rows, void* ws,
+                   bool store_gu, hipStream_t s) {
+  GemmArgs g = {};
+  set_a_linear(g, static_cast<const uint16_t*>(x) + r0 * p.H, rows, p.H);
+  set_b_linear(g, Wgu, 2 * p.I, p.H);
+  g.M = rows;
+  g.N = 2 * p.I;
+  g.kchunk = p.H;
+  g.ksplit = 1;
+  g.alpha = 1.f;
+  if (store_gu) {
+    g.epi = kEpiStoreBf16;
+    g.C = at<uint16_t>(ws, p.off_gu);
+    g.ldc = 2 * p.I;
+  } else {
+    g.epi = kEpiSwigluFwd;
+    g.C = at<uint16_t>(ws, p.off_act);
+    g.ldc = p.I;
+  }
+  g.patch_m = 4;
+  return launch_gemm(g, s);
+}
+
+// Packs Wg, Wu and writes the K-tiled transposes the backward reads.
+hipError_t prepare_weights(const MlpPlan& p, const void* Wg, const void* Wu, const void* Wd, void* ws, bool bwd,
+                           hipStream_t s) {
+  uint16_t* Wgu = at<uint16_t>(ws, p.off_Wgu);
+  hipLaunchKernelGGL(k_pack_gu, dim3((unsigned)(2 * p.I)), dim3(256), 0, s, static_cast<const uint16_t*>(Wg),
+                     static_cast<const uint16_t*>(Wu), p.H, Wgu);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !bwd) return e;
+  e = launch_transpose(Wgu, 2 * p.I, p.H, at<uint16_t>(ws, p.off_WguT), 2 * p.I, s);
+  if (e != hipSuccess) return e;
+  return launch_transpose(Wd, p.H, p.I, at<uint16_t>(ws, p.off_WdT), p.H, s);
+}
+
+}  // namespace
+}  // namespace lmce
+
+using namespace lmce;
+
+extern "C" int lmce_mlp_workspace_size(int64_t L, int64_t H, int64_t I, int64_t chunk_rows, size_t* bytes) {
+  if (bytes == nullptr) return LMCE_ERR_NULL;
+  MlpPlan p;
+  const int st = mlp_plan(L, H, I, chunk_rows, &p);
+  if (st != LMCE_OK) return st;
+  *bytes = p.total;
+  return LMCE_OK;
+}
+
+extern "C" int lmce_mlp_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd, int64_t L, int64_t H,
+                            int64_t I, int64_t chunk_rows, float* y_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  MlpPlan p;
+  int st = mlp_plan(L, H, I, chunk_rows, &p);
+  if (st != LMCE_OK) return st;
+  if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(y_out, 16) ||
+      !aligned(workspace, 256))
+    return LMCE_ERR_NULL;
+  if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (prepare_weights(p, Wg, Wu, Wd, workspace, false, s) != hipSuccess) return LMCE_ERR_HIP;
+  const uint16_t* Wgu = at<uint16_t>(workspace, p.off_Wgu);
+  for (int64_t r0 = 0; r0 < L; r0 += p.cr) {
+    const int64_t rows = (L - r0) < p.cr ? (L - r0) : p.cr;
+    if (gate_up(p, x, Wgu, r0, rows, workspace, false, s) != hipSuccess) return LMCE_ERR_HIP;
+    GemmArgs g = {};
+    set_a_linear(g, at<uint16_t>(workspace, p.off_act), rows, I);
+    set_b_linear(g, Wd, H, I);
+    g.M = rows;
+    g.N = H;
+    g.kchunk = I;
+    g.ksplit = 1;
+    g.epi = kEpiStoreF32;
+    g.alpha = 1.f;
+    g.C = y_out + r0 * H;
+    g.ldc = H;
+    g.patch_m = 4;
+    if (launch_gemm(g, s) != hipSuccess) return LMCE_ERR_HIP;
+  }
+  return LMCE_OK;
+}
+
+extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd, const void* dy, int64_t L,
+                            int64_t H, int64_t I, int64_t chunk_rows, float* dx_out, float* dWg_out, float* dWu_out,
+                            float* dWd_out, void* workspace, size_t workspace_bytes, void* stream) {
+  MlpPlan p;
+  int st = mlp_plan(L, H, I, chunk_rows, &p);
+  if (st != LMCE_OK) return st;
+  if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(dy, 16) ||
+      !aligned(dx_out, 16) || !aligned(dWg_out, 16) || !aligned(dWu_out, 16) || !aligned(dWd_out, 16) ||
+      !aligned(workspace, 256))
+    return LMCE_ERR_NULL;
+  if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (prepare_weights(p, Wg, Wu, Wd, workspace, true, s) != hipSuccess) return LMCE_ERR_HIP;
+  // the weight gradients are sums over the chunks: start from zero (a fill
+  // kernel, which graph capture records as an ordinary node)
+  if (launch_zero_u32(reinterpret_cast<unsigned*>(dWg_out), (int)(I * H), s) != hipSuccess ||
+      launch_zero_u32(reinterpret_cast<unsigned*>(dWu_out), (int)(I * H), s) != hipSuccess ||
+      launch_zero_u32(reinterpret_cast<unsigned*>(dWd_out), (int)(H * I), s) != hipSuccess)
+    return LMCE_ERR_HIP;
+  const uint16_t* Wgu = at<uint16_t>(workspace, p.off_Wgu);
+  uint16_t* gu = at<uint16_t>(workspace, p.off_gu);
+  uint16_t* act = at<uint16_t>(workspace, p.off_act);
+  uint16_t* dgu = at<uint16_t>(workspace, p.off_dgu);
+  uint16_t* actT = at<uint16_t>(workspace, p.off_actT);
+  uint16_t* dguT = at<uint16_t>(workspace, p.off_dguT);
+  uint16_t* dyT = at<uint16_t>(workspace, p.off_dyT);
+  uint16_t* xT = at<uint16_t>(workspace, p.off_xT);
+  const uint16_t* x16 = static_cast<const uint16_t*>(x);
+  const uint16_t* dy16 = static_cast<const uint16_t*>(dy);
+  for (int64_t r0 = 0; r0 < L; r0 += p.cr) {
+    const int64_t rows = (L - r0) < p.cr ? (L - r0) : p.cr;
+    const int64_t rp = (rows + 127) / 128 * 128;
+    if (gate_up(p, x, Wgu, r0, rows, workspace, true, s) != hipSuccess) return LMCE_ERR_HIP;
+    // dp = dy_c Wd (B = Wd^T, K = H), epilogue: dg, du (packed like gu) and p
+    GemmArgs d = {};
+    set_a_linear(d, dy16 + r0 * H, rows, H);
+    set_b_tiled(d, at<uint16_t>(workspace, p.off_WdT), I, H);
+    d.M = rows;
+    d.N = I;
+    d.kchunk = H;
+    d.ksplit = 1;
+    d.epi = kEpiSwigluBwd;
+    d.alpha = 1.f;
+    d.C = dgu;
+    d.gu = gu;
+    d.aux = act;
+    d.ld_aux = I;
+    d.patch_m = 4;
+    if (launch_gemm(d, s) != hipSuccess) return LMCE_ERR_HIP;
+    // dx_c = [dg | du] [Wg; Wu] (B = the packed matrix transposed, K = 2I)
+    GemmArgs xg = {};
+    set_a_linear(xg, dgu, rows, 2 * I);
+    set_b_tiled(xg, at<uint16_t>(workspace, p.off_WguT), H, 2 * I);
+    xg.M = rows;
+    xg.N = H;
+    xg.kchunk = 2 * I;
+    xg.ksplit = 1;
+    xg.epi = kEpiStoreF32;
+    xg.alpha = 1.f;
+    xg.C = dx_out + r0 * H;
+    xg.ldc = H;
+    xg.patch_m = 4;
+    if (launch_gemm(xg, s) != hipSuccess) return LMCE_ERR_HIP;
+    // weight gradients: K = the chunk's rows, from K-tiled transposes (zero past `rows`)
+    if (launch_transpose(act, rows, I, actT, rp, s) != hipSuccess ||
+        launch_transpose(dgu, rows, 2 * I, dguT, rp, s) != hipSuccess ||
+        launch_transpose(dy16 + r0 * H, rows, H, dyT, rp, s) != hipSuccess ||
+        launch_transpose(x16 + r0 * H, rows, H, xT, rp, s) != hipSuccess)
+      return LMCE_ERR_HIP;
+    GemmArgs wd = {};
+    set_a_tiled(wd, dyT, H, rp);
+    set_b_tiled(wd, actT, I, rp);
+    wd.M = H;
+    wd.N = I;
+    wd.kchunk = rp;
+    wd.ksplit = 1;
+    wd.epi = kEpiAccF32;
+    wd.alpha = 1.f;
+    wd.C = dWd_out;
+    wd.ldc = I;
+    wd.patch_m = 4;
+    if (launch_gemm(wd, s) != hipSuccess) return LMCE_ERR_HIP;
+    GemmArgs wg = {};
+    set_a_tiled(wg, dguT, 2 * I, rp);
+    set_b_tiled(wg, xT, H, rp);
+    wg.M = 2 * I;
+    wg.N = H;
+    wg.kchunk = rp;
+    wg.ksplit = 1;
+    wg.epi = kEpiAccF32Gu;
+    wg.alpha = 1.f;
+    wg.C = dWg_out;
+    wg.C2 = dWu_out;
+    wg.ldc = H;
+    wg.patch_m = 4;
+    if (launch_gemm(wg, s) != hipSuccess) return LMCE_ERR_HIP;
+  }
+  return LMCE_OK;
+}
