@@ -300,7 +300,7 @@ def main():
                   lambda: lm.lmce_chunked_bwd(h, W, y, g, -100, chunk, ws, dh, dW))]
     else:
         calls = [("lmce_fwd_train", "k_fwd_dh", f_fwd + 2 * f_nhv,
-                  lambda: lm.lmce_fwd_train(h, W, y, -100, chunk, ws, loss, lse)),
+                  lambda: lm.lmce_fwd_train(h, W, y, -100, chunk, ws, loss, lse, dh)),
                  ("lmce_bwd_train", "k_bwd_dW", 4 * f_nhv,
                   lambda: lm.lmce_bwd_train(h, W, y, lse, g, -100, chunk, ws, dh, dW))]
 

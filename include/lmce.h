@@ -70,12 +70,14 @@ int lmce_version(void);
 const char* lmce_strerror(int status);
 
 /*
- * Bytes of device workspace that lmce_fwd / lmce_bwd need for this shape:
- * transposed bf16 copies of h and W for the backward ((L + V) * H * 2 bytes,
- * rounded up to 128 rows), per-row forward partials (O(L) floats), a fixed
- * exchange ring for the backward (at most 64 MiB) and, for H >= 3072, a
- * parking area for backward accumulators (at most 64 MiB), and the training
- * forward's O (L * H * 4 bytes).  It never holds an L x V array.  Writes the size to *bytes.  Returns LMCE_OK or a shape error.
+ * Bytes of device workspace that lmce_fwd / lmce_bwd and the training pair
+ * need for this shape: transposed bf16 copies of h and W for the backward
+ * ((L + V) * H * 2 bytes, rounded up to 128 rows), per-row partials and
+ * orders (O(L) words), a fixed exchange ring for the group passes (at most
+ * 64 MiB), for H >= 3072 a parking area for their accumulators (at most
+ * 64 MiB), and the dW pass's partial slices (at most 64 MiB).  It never holds
+ * an L x V array.  Writes the size to *bytes.  Returns LMCE_OK or a shape
+ * error.
  */
 int lmce_workspace_size(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, size_t* bytes);
 
@@ -165,20 +167,23 @@ int lmce_bwd_dW(const void* h, const void* W, const int64_t* labels, const float
  * by lmce_bwd, with less work: the forward's single vocabulary sweep also
  * accumulates O_i = sum_v softmax(z_i)_v W_v with a running-maximum rescale
  * (the gradient of the mean NLL is dh_i = g/N * valid_i * (O_i - W_{y_i})),
- * and keeps O (fp32 [L, H]) in the workspace.  lmce_bwd_train then forms dh
- * from O without recomputing any logit and runs the dW pass.
+ * and writes O (fp32 [L, H]) into the caller's dh_out.  lmce_bwd_train then
+ * forms dh in place in that buffer without recomputing any logit, and runs
+ * the dW pass.  Between the two calls the buffer holds O, not dh.
  *
- * lmce_fwd_train: arguments and outputs as lmce_fwd.
- * lmce_bwd_train: arguments and outputs as lmce_bwd.  It must follow an
- *   lmce_fwd_train on the same inputs, workspace and stream, with no other
- *   lmce_fwd in between; otherwise dh_out is NaN and lmce_read_status()
+ * lmce_fwd_train: arguments and outputs as lmce_fwd, plus dh_out (fp32
+ *   [L, H], 16-byte aligned), which receives O.
+ * lmce_bwd_train: arguments and outputs as lmce_bwd; dh_out must be the
+ *   buffer the preceding lmce_fwd_train wrote O into, on the same inputs,
+ *   workspace and stream, with no other lmce_fwd or lmce_fwd_train on the
+ *   workspace in between; otherwise dh_out is NaN and lmce_read_status()
  *   returns LMCE_ERR_STATE.  Calls of lmce_bwd, lmce_bwd_dh or lmce_bwd_dW
  *   on the workspace in between, with any inputs, are allowed: they leave
  *   the training forward's state alone.
  */
 int lmce_fwd_train(const void* h, const void* W, const int64_t* labels,
                    int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,
-                   float* loss_out, float* lse_out,
+                   float* loss_out, float* lse_out, float* dh_out,
                    void* workspace, size_t workspace_bytes, void* stream);
 int lmce_bwd_train(const void* h, const void* W, const int64_t* labels, const float* lse,
                    int64_t L, int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_rows,

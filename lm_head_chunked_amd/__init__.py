@@ -107,9 +107,11 @@ def lmce_fwd_noalloc(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT
 
 
 def lmce_fwd_train(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS, workspace=None,
-                   loss_out=None, lse_out=None):
-    """As lmce_fwd, and also leaves in `workspace` what lmce_bwd_train needs
-    to form dh without recomputing the logits.  Pass the same workspace on."""
+                   loss_out=None, lse_out=None, dh_out=None):
+    """As lmce_fwd, and also writes into dh_out (fp32 [L, H], allocated if
+    None) what lmce_bwd_train needs to form dh there without recomputing the
+    logits.  Returns (loss, lse, dh_buffer); pass the same workspace and
+    dh_buffer on to lmce_bwd_train."""
     L, H, V = _check_inputs(h, W, labels)
     dev = h.device
     if workspace is None:
@@ -117,26 +119,34 @@ def lmce_fwd_train(h, W, labels, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_C
     ws = _workspace(L, H, V, chunk_rows, dev, workspace)
     loss = torch.empty((), dtype=torch.float32, device=dev) if loss_out is None else loss_out
     lse = torch.empty(L, dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    dh = torch.empty(L, H, dtype=torch.float32, device=dev) if dh_out is None else dh_out
+    if dh.dtype != torch.float32 or dh.shape != (L, H) or not dh.is_contiguous():
+        raise ValueError("dh_out must be contiguous fp32 [L, H]")
     st = _lib.fwd_train(h.data_ptr(), W.data_ptr(), labels.data_ptr(), L, H, V, ignore_index, chunk_rows,
-                        loss.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev))
+                        loss.data_ptr(), lse.data_ptr(), dh.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                        _stream(dev))
     _lib.check(st, "lmce_fwd_train")
-    return loss, lse
+    return loss, lse, dh
 
 
 def lmce_bwd_train(h, W, labels, lse, grad_loss=None, ignore_index=IGNORE_INDEX, chunk_rows=DEFAULT_CHUNK_ROWS,
                    workspace=None, dh_out=None, dW_out=None):
-    """dh and dW like lmce_bwd, after lmce_fwd_train on the same inputs and workspace."""
+    """dh and dW like lmce_bwd, after lmce_fwd_train on the same inputs and
+    workspace; dh_out must be the dh buffer that lmce_fwd_train returned (dh
+    is formed in place there)."""
     L, H, V = _check_inputs(h, W, labels)
     dev = h.device
     if lse.dtype != torch.float32 or lse.shape != (L,) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [L]")
-    if workspace is None:
-        raise ValueError("lmce_bwd_train needs the workspace of lmce_fwd_train")
+    if workspace is None or dh_out is None:
+        raise ValueError("lmce_bwd_train needs the workspace and the dh buffer of lmce_fwd_train")
     if grad_loss is None:
         grad_loss = torch.ones((), dtype=torch.float32, device=dev)
     grad_loss = grad_loss.to(device=dev, dtype=torch.float32).contiguous()
     ws = _workspace(L, H, V, chunk_rows, dev, workspace)
-    dh = torch.empty(L, H, dtype=torch.float32, device=dev) if dh_out is None else dh_out
+    dh = dh_out
+    if dh.dtype != torch.float32 or dh.shape != (L, H) or not dh.is_contiguous():
+        raise ValueError("dh_out must be contiguous fp32 [L, H]")
     dW = torch.empty(V, H, dtype=torch.float32, device=dev) if dW_out is None else dW_out
     st = _lib.bwd_train(h.data_ptr(), W.data_ptr(), labels.data_ptr(), lse.data_ptr(), L, H, V, ignore_index,
                         chunk_rows, grad_loss.data_ptr(), dh.data_ptr(), dW.data_ptr(), ws.data_ptr(),
@@ -308,18 +318,20 @@ class _ChunkedNLL(torch.autograd.Function):
     def forward(ctx, h, W, labels, ignore_index, chunk_rows):
         L, H, V = _check_inputs(h, W, labels)
         ws = _workspace(L, H, V, chunk_rows, h.device, None)
-        loss, lse = lmce_fwd_train(h, W, labels, ignore_index, chunk_rows, ws)
+        loss, lse, dh = lmce_fwd_train(h, W, labels, ignore_index, chunk_rows, ws)
         ctx.save_for_backward(h, W, labels, lse)
         ctx.ignore_index = ignore_index
         ctx.chunk_rows = chunk_rows
         ctx.ws = ws
+        ctx.dh = dh
         return loss
 
     @staticmethod
     def backward(ctx, grad_loss):
         h, W, labels, lse = ctx.saved_tensors
-        dh, dW = lmce_bwd_train(h, W, labels, lse, grad_loss, ctx.ignore_index, ctx.chunk_rows, ctx.ws)
+        dh, dW = lmce_bwd_train(h, W, labels, lse, grad_loss, ctx.ignore_index, ctx.chunk_rows, ctx.ws, ctx.dh)
         ctx.ws = None
+        ctx.dh = None
         return dh, dW, None, None, None
 
 

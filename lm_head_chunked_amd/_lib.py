@@ -39,7 +39,7 @@ SIGNATURES = {
     "lmce_bwd_dW": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                    _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_fwd_train": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
-                                      _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+                                      _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_bwd_train": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                       _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "lmce_read_status": (ctypes.c_int, [_c_vp, _c_vp]),
@@ -121,10 +121,10 @@ def bwd_dW(h_ptr, W_ptr, labels_ptr, lse_ptr, L, H, V, ignore_index, chunk_rows,
                               int(chunk_rows), grad_ptr, dW_ptr, ws_ptr, int(ws_bytes), stream)
 
 
-def fwd_train(h_ptr, W_ptr, labels_ptr, L, H, V, ignore_index, chunk_rows, loss_ptr, lse_ptr, ws_ptr, ws_bytes,
-              stream):
+def fwd_train(h_ptr, W_ptr, labels_ptr, L, H, V, ignore_index, chunk_rows, loss_ptr, lse_ptr, dh_ptr, ws_ptr,
+              ws_bytes, stream):
     return load().lmce_fwd_train(h_ptr, W_ptr, labels_ptr, int(L), int(H), int(V), int(ignore_index),
-                                 int(chunk_rows), loss_ptr, lse_ptr, ws_ptr, int(ws_bytes), stream)
+                                 int(chunk_rows), loss_ptr, lse_ptr, dh_ptr, ws_ptr, int(ws_bytes), stream)
 
 
 def bwd_train(h_ptr, W_ptr, labels_ptr, lse_ptr, L, H, V, ignore_index, chunk_rows, grad_ptr, dh_ptr, dW_ptr, ws_ptr,

@@ -37,7 +37,7 @@ struct Plan {
   int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
   int64_t Lpad, Vpad;
   int hs, xbuf_wgs;
-  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, off_xstat, off_O, off_cnt, off_crow,
+  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, off_xstat, off_cnt, off_crow,
       off_clab, off_clse, off_part, off_fperm, off_finv, total;
 };
 
@@ -102,9 +102,6 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   if (p->hs == 256) off = align256(off + (size_t)wgs * kParkPerWG);
   p->off_xstat = off;
   off = align256(off + (size_t)wgs * kXstatPerWG);
-  // training forward: O = sum_v softmax(z)_v W_v of every row, fp32 [L][H]
-  p->off_O = off;
-  off = align256(off + sizeof(float) * (size_t)L * (size_t)H);
   // dW pass on the labelled rows only: per-chunk counts, then their index,
   // label and lse (their h rows go to the W^T area, free during that pass)
   p->off_cnt = off;
@@ -362,7 +359,6 @@ BwdArgs group_args(const Plan& p, const void* h, const void* W, const int64_t* l
   a.xbuf = at<uint16_t>(workspace, p.off_xbuf);
   a.park = at<float>(workspace, p.off_park);
   a.xstat = at<float>(workspace, p.off_xstat);
-  a.O = at<float>(workspace, p.off_O);
   a.part_m = at<float>(workspace, p.off_pm);
   a.part_s = at<float>(workspace, p.off_ps);
   a.hdr = at<WsHeader>(workspace, 0);
@@ -447,12 +443,12 @@ extern "C" int lmce_bwd_dW(const void* h, const void* W, const int64_t* labels, 
 
 extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* labels, int64_t L, int64_t H, int64_t V,
                               int64_t ignore_index, int64_t chunk_rows, float* loss_out, float* lse_out,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              float* dh_out, void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
   int st = make_plan(L, H, V, chunk_rows, &p);
   if (st != LMCE_OK) return st;
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(labels, 8) || !aligned(loss_out, 4) || !aligned(lse_out, 4) ||
-      !aligned(workspace, 256))
+      !aligned(dh_out, 16) || !aligned(workspace, 256))
     return LMCE_ERR_NULL;
   if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -462,6 +458,7 @@ extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* label
   WsHeader* hdr = at<WsHeader>(workspace, 0);
   if (launch_count_labels(labels, L, V, ignore_index, hdr, 0, s) != hipSuccess) return LMCE_ERR_HIP;
   BwdArgs a = group_args(p, h, W, labels, ignore_index, workspace);
+  a.O = dh_out;  // O rows live in the caller's dh buffer until lmce_bwd_train turns them into dh
   if (launch_permute(a, at<int>(workspace, p.off_cnt), &hdr->fcompact, a.fperm, a.finv, s) != hipSuccess)
     return LMCE_ERR_HIP;
   if (launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
@@ -483,7 +480,7 @@ extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* label
   f.part_s = a.part_s;
   f.block_sum = at<float>(workspace, p.off_bsum);
   f.finv = a.finv;
-  if (launch_fwd_rows(f, loss_out, lse_out, s, true) != hipSuccess) return LMCE_ERR_HIP;
+  if (launch_fwd_rows(f, loss_out, lse_out, s, true, dh_out) != hipSuccess) return LMCE_ERR_HIP;
   return LMCE_OK;
 }
 

@@ -938,25 +938,28 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) fin[mb][nb][reg] *= a;
       }
-    store_tile_f32(p.O + r0 * H + c0, L - r0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
+    // O rows go to their row of the caller's buffer (through the order, if any)
+    if (reordered) store_rows_perm<C::MB, C::NB, false>(p.O, p.fperm, r0, L, H, c0, fin, wm * 64, wn * (HS / 2), lane);
+    else store_tile_f32(p.O + r0 * H + c0, L - r0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
   }
 }
 
-// dh = g/N * (O - W_y) for rows with a label, 0 for the others; NaN (and the
-// state flag) if the workspace does not hold a complete training forward's O
-// (none ran, another forward ran since, or one of its group waits gave up).
+// dh = g/N * (O - W_y) for rows with a label, 0 for the others, in place in
+// the buffer that holds O (row r of O is row r of dh: each element is read,
+// then overwritten by the same thread); NaN (and the state flag) if that
+// buffer does not hold a complete training forward's O (none ran, another
+// forward ran since, one of its group waits gave up, or the forward wrote O
+// into another buffer).
 __global__ __launch_bounds__(256) void k_dh_finish(BwdArgs p) {
   const int64_t r = blockIdx.x;
   const int64_t H = p.H;
   const int64_t y = p.labels[r];
   const bool valid = y != p.ignore_index && y >= 0 && y < p.V;
-  const bool ok = p.hdr->saved == kSavedTag;
+  const bool ok = p.hdr->saved == kSavedTag && p.hdr->o_addr == (unsigned long long)(uintptr_t)p.dh;
   const int n = p.hdr->n_valid;
   const float scale = *p.grad_loss / (float)(n > 0 ? n : 1);
   if (!ok && r == 0 && threadIdx.x == 0)
     __hip_atomic_fetch_or(&p.hdr->status, kStatusState, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int64_t orow = p.hdr->fcompact ? (int64_t)p.finv[r] : r;  // O is indexed by the forward's row order
-  const float4* o = reinterpret_cast<const float4*>(p.O + orow * H);
   const u16* w = p.W + (valid ? y : 0) * H;
   float4* d = reinterpret_cast<float4*>(p.dh + r * H);
   for (int64_t c = threadIdx.x; c < H / 4; c += 256) {
@@ -964,7 +967,7 @@ __global__ __launch_bounds__(256) void k_dh_finish(BwdArgs p) {
     if (!ok) {
       v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
     } else if (valid) {
-      const float4 ov = o[c];
+      const float4 ov = d[c];
       const bf16x4 wv = *reinterpret_cast<const bf16x4*>(w + c * 4);
       v = make_float4(scale * (ov.x - (float)wv[0]), scale * (ov.y - (float)wv[1]), scale * (ov.z - (float)wv[2]),
                       scale * (ov.w - (float)wv[3]));

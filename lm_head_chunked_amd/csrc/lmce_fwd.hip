@@ -243,7 +243,8 @@ __global__ __launch_bounds__(256) void k_fwd_rows(FwdArgs p, float* __restrict__
 // saw a bad label or a group wait that gave up.  train: the last kernel of the
 // training forward, which marks the workspace as holding a complete O only
 // when none of its group waits gave up.
-__global__ __launch_bounds__(256) void k_fwd_loss(FwdArgs p, int nblocks, float* __restrict__ loss_out, int train) {
+__global__ __launch_bounds__(256) void k_fwd_loss(FwdArgs p, int nblocks, float* __restrict__ loss_out, int train,
+                                                  const float* o_buf) {
   __shared__ float red[256];
   float acc = 0.f;
   for (int i = threadIdx.x; i < nblocks; i += 256) acc += p.block_sum[i];
@@ -259,7 +260,10 @@ __global__ __launch_bounds__(256) void k_fwd_loss(FwdArgs p, int nblocks, float*
     float loss = (n > 0) ? red[0] / (float)n : __builtin_nanf("");
     if (flags != 0) loss = __builtin_nanf("");
     *loss_out = loss;
-    if (train) p.hdr->saved = (flags & kStatusSync) ? 0 : kSavedTag;
+    if (train) {
+      p.hdr->o_addr = (unsigned long long)(uintptr_t)o_buf;
+      p.hdr->saved = (flags & kStatusSync) ? 0 : kSavedTag;
+    }
   }
 }
 
@@ -280,13 +284,14 @@ hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStre
 
 // Merges the per-segment (max, sum) partials of every row into lse, forms
 // nll and the loss.
-hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st, bool train) {
+hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st, bool train,
+                           const float* o_buf) {
   hipError_t e;
   const int nblocks = (int)((a.L + 63) / 64);
   hipLaunchKernelGGL(k_fwd_rows, dim3(nblocks), dim3(256), 0, st, a, lse_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_fwd_loss, dim3(1), dim3(256), 0, st, a, nblocks, loss_out, train ? 1 : 0);
+  hipLaunchKernelGGL(k_fwd_loss, dim3(1), dim3(256), 0, st, a, nblocks, loss_out, train ? 1 : 0, o_buf);
   return hipGetLastError();
 }
 

@@ -33,7 +33,9 @@ struct WsHeader {
   int d_n;       // labelled rows of that order
   int tag;       // kHdrTag once k_count_labels has initialised status and saved
   int call_flags;  // flags raised by the current entry point only (cleared when it starts)
-  int pad[53];
+  int pad0;
+  unsigned long long o_addr;  // device address of the buffer the training forward wrote O into
+  int pad[50];
 };
 static_assert(sizeof(WsHeader) == 256, "the header is the first 256 bytes of the workspace");
 
@@ -74,7 +76,8 @@ struct BwdArgs {
   uint16_t* xbuf;       // [n_groups][2][2 * group_size][256][128] exchange slots
   float* park;          // [workgroups][256 x 256] parked accumulators (HS = 256 only)
   float* xstat;         // [n_groups][3][group_size][256] round maxima (2 slots) and final sums, fused forward
-  float* O;             // [L][H] normalised sum_v softmax(z)_v W_v, fused forward output
+  float* O;             // [L][H] normalised sum_v softmax(z)_v W_v by row: the fused forward's output, written into
+                        // the caller's dh buffer
   float* part_m;        // [L] row max, fused forward output
   float* part_s;        // [L] row sum of exp(z - max), fused forward output
   WsHeader* hdr;
@@ -148,7 +151,8 @@ hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int6
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);
 // train: the training forward, whose last kernel sets the saved tag when its
 // group waits all succeeded.
-hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st, bool train = false);
+hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st, bool train = false,
+                           const float* o_buf = nullptr);
 hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st);
 // Compaction of the labelled rows for the dW pass (cnt: ceil(L / 1024) ints),
 // then h^T of the rows the dW pass sweeps (compacted or all L).

@@ -29,6 +29,7 @@ import oracle
 import lm_head_chunked_amd as lm
 from lm_head_chunked_amd import _lib, synth
 from tests.golden.make_full_golden import LONG, digest, golden_paths
+from tests.pairs import run_pair
 
 pytestmark = pytest.mark.gpu
 
@@ -47,11 +48,6 @@ def np32(t):
 
 def rel_fro(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
-
-
-def pair(train):
-    """The plain pair, or the training pair that bench.py times."""
-    return (lm.lmce_fwd_train, lm.lmce_bwd_train) if train else (lm.lmce_fwd, lm.lmce_bwd)
 
 
 _cache = {}
@@ -81,9 +77,7 @@ def test_full_size_against_full_oracle(name, train):
     dev = torch.device("cuda:0")
     h, W, y = h_c.to(dev), W_c.to(dev), y_c.to(dev)
     ws = torch.empty(lm.lmce_workspace_size(wl.L, wl.H, wl.V, 256), dtype=torch.uint8, device=dev)
-    fwd, bwd = pair(train)
-    loss, lse = fwd(h, W, y, -100, 256, ws)
-    dh, dW = bwd(h, W, y, lse, None, -100, 256, ws)
+    loss, lse, dh, dW = run_pair(train, h, W, y, -100, 256, ws)
     assert lm.lmce_read_status(ws) == _lib.LMCE_OK
     torch.cuda.synchronize()
     del ws
@@ -131,9 +125,7 @@ def test_reduced_rows_full_parity(name, train):
     h = h[:Lr].contiguous()
     y = y[:Lr].contiguous()
     ws = torch.empty(lm.lmce_workspace_size(Lr, wl.H, wl.V, 256), dtype=torch.uint8, device=dev)
-    fwd, bwd = pair(train)
-    loss, lse = fwd(h, W, y, -100, 256, ws)
-    dh, dW = bwd(h, W, y, lse, None, -100, 256, ws)
+    loss, lse, dh, dW = run_pair(train, h, W, y, -100, 256, ws)
     assert lm.lmce_read_status(ws) == _lib.LMCE_OK
     torch.cuda.synchronize()
     ref = oracle.fwd_bwd(np32(h), np32(W), y.cpu().numpy())

@@ -16,6 +16,7 @@ import torch
 import oracle
 import lm_head_chunked_amd as lm
 from lm_head_chunked_amd import _lib, synth
+from tests.pairs import run_pair
 
 pytestmark = pytest.mark.gpu
 
@@ -44,10 +45,8 @@ def run_gpu(h, W, y, chunk_rows=256, grad=1.0, ignore_index=-100, train=False):
     L, H = h.shape
     V = W.shape[0]
     ws = torch.empty(lm.lmce_workspace_size(L, H, V, chunk_rows), dtype=torch.uint8, device=dev)
-    fwd, bwd = (lm.lmce_fwd_train, lm.lmce_bwd_train) if train else (lm.lmce_fwd, lm.lmce_bwd)
-    loss, lse = fwd(h_d, W_d, y_d, ignore_index, chunk_rows, ws)
     g = torch.tensor(grad, dtype=torch.float32, device=dev)
-    dh, dW = bwd(h_d, W_d, y_d, lse, g, ignore_index, chunk_rows, ws)
+    loss, lse, dh, dW = run_pair(train, h_d, W_d, y_d, ignore_index, chunk_rows, ws, g)
     status = lm.lmce_read_status(ws)
     torch.cuda.synchronize()
     return {"loss": float(loss), "lse": lse.cpu().numpy(), "dh": dh.cpu().numpy(), "dW": dW.cpu().numpy(),
@@ -273,14 +272,20 @@ def test_train_backward_without_train_forward_is_reported():
     hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
     ws = torch.empty(lm.lmce_workspace_size(256, 128, 600), dtype=torch.uint8, device=dev)
     loss, lse = lm.lmce_fwd(hd, Wd, yd, workspace=ws)
-    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws, dh_out=torch.empty(256, 128, device=dev))
     assert lm.lmce_read_status(ws) == _lib.LMCE_ERR_STATE
     assert torch.isnan(dh).all()
     # a training forward on the same workspace makes the pair valid again
-    loss, lse = lm.lmce_fwd_train(hd, Wd, yd, workspace=ws)
-    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws)
+    loss, lse, dh = lm.lmce_fwd_train(hd, Wd, yd, workspace=ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws, dh_out=dh)
     assert lm.lmce_read_status(ws) == _lib.LMCE_OK
     assert torch.isfinite(dh).all()
+    # ... but only in the buffer the forward wrote O into
+    loss, lse, dh = lm.lmce_fwd_train(hd, Wd, yd, workspace=ws)
+    other = torch.zeros_like(dh)
+    lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws, dh_out=other)
+    assert lm.lmce_read_status(ws) == _lib.LMCE_ERR_STATE
+    assert torch.isnan(other).all()
 
 
 def test_results_do_not_depend_on_chunk_rows():
@@ -326,12 +331,10 @@ def test_workspace_contents_do_not_matter(L, H, V, ign, train):
     h, W, y = synth.random_case(L, H, V, seed=L + 2 * V, w_std=0.05, ignore_frac=ign)
     dev = torch.device("cuda:0")
     hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
-    fwd, bwd = (lm.lmce_fwd_train, lm.lmce_bwd_train) if train else (lm.lmce_fwd, lm.lmce_bwd)
     outs = []
     for fill in (0x00, 0xFF):
         ws = torch.full((lm.lmce_workspace_size(L, H, V, 256),), fill, dtype=torch.uint8, device=dev)
-        loss, lse = fwd(hd, Wd, yd, -100, 256, ws)
-        dh, dW = bwd(hd, Wd, yd, lse, None, -100, 256, ws)
+        loss, lse, dh, dW = run_pair(train, hd, Wd, yd, -100, 256, ws)
         assert lm.lmce_read_status(ws) == _lib.LMCE_OK
         outs.append((float(loss), lse.cpu().numpy(), dh.cpu().numpy(), dW.cpu().numpy()))
     assert np.isfinite(outs[1][0]) and all(np.isfinite(x).all() for x in outs[1][1:])
@@ -352,13 +355,13 @@ def test_plain_backward_between_train_calls_leaves_the_saved_forward():
     dev = torch.device("cuda:0")
     hd, Wd, yd, y2d = h.to(dev), W.to(dev), y.to(dev), y2.to(dev)
     ws = torch.empty(lm.lmce_workspace_size(L, H, V, 256), dtype=torch.uint8, device=dev)
-    loss, lse = lm.lmce_fwd_train(hd, Wd, yd, -100, 256, ws)
-    dh_ref, dW_ref = lm.lmce_bwd_train(hd, Wd, yd, lse, None, -100, 256, ws)
+    loss, lse, dh0 = lm.lmce_fwd_train(hd, Wd, yd, -100, 256, ws)
+    dh_ref, dW_ref = lm.lmce_bwd_train(hd, Wd, yd, lse, None, -100, 256, ws, dh0)
     ref = (dh_ref.cpu().numpy(), dW_ref.cpu().numpy())
-    loss, lse = lm.lmce_fwd_train(hd, Wd, yd, -100, 256, ws)
+    loss, lse, dh1 = lm.lmce_fwd_train(hd, Wd, yd, -100, 256, ws)
     _, lse2 = lm.lmce_fwd(hd, Wd, y2d, -100, 256, torch.empty_like(ws))
     dh2, dW2 = lm.lmce_bwd(hd, Wd, y2d, lse2, None, -100, 256, ws)
-    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, None, -100, 256, ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, None, -100, 256, ws, dh1)
     assert lm.lmce_read_status(ws) == _lib.LMCE_OK
     assert np.array_equal(dh.cpu().numpy(), ref[0]) and np.array_equal(dW.cpu().numpy(), ref[1])
     # and the plain backward itself, on the other labels
@@ -508,15 +511,15 @@ def test_failed_group_wait_survives_the_following_backward():
     dev = torch.device("cuda:0")
     hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
     ws = torch.empty(lm.lmce_workspace_size(L, H, V), dtype=torch.uint8, device=dev)
-    loss, lse = _with_spin_limit(0, lambda: lm.lmce_fwd_train(hd, Wd, yd, workspace=ws))
+    loss, lse, dh = _with_spin_limit(0, lambda: lm.lmce_fwd_train(hd, Wd, yd, workspace=ws))
     torch.cuda.synchronize()
-    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws, dh_out=dh)
     assert lm.lmce_read_status(ws) == _lib.LMCE_ERR_HIP
     assert math.isnan(float(loss))
     assert torch.isnan(dh).all()
     assert lm.lmce_read_status(ws) == _lib.LMCE_OK  # the read cleared the flags
-    loss, lse = lm.lmce_fwd_train(hd, Wd, yd, workspace=ws)
-    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws)
+    loss, lse, dh = lm.lmce_fwd_train(hd, Wd, yd, workspace=ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, yd, lse, workspace=ws, dh_out=dh)
     assert lm.lmce_read_status(ws) == _lib.LMCE_OK
     ref = oracle.fwd_bwd(np32(h), np32(W), y.numpy())
     gpu = {"loss": float(loss), "lse": lse.cpu().numpy(), "dh": dh.cpu().numpy(), "dW": dW.cpu().numpy(),
@@ -550,8 +553,8 @@ def test_label_error_accumulates_until_read():
     hd, Wd = h.to(dev), W.to(dev)
     ws = torch.empty(lm.lmce_workspace_size(300, 128, 700), dtype=torch.uint8, device=dev)
     loss_bad, _ = lm.lmce_fwd(hd, Wd, ybad.to(dev), workspace=ws)
-    loss, lse = lm.lmce_fwd_train(hd, Wd, y.to(dev), workspace=ws)
-    dh, dW = lm.lmce_bwd_train(hd, Wd, y.to(dev), lse, workspace=ws)
+    loss, lse, dh = lm.lmce_fwd_train(hd, Wd, y.to(dev), workspace=ws)
+    dh, dW = lm.lmce_bwd_train(hd, Wd, y.to(dev), lse, workspace=ws, dh_out=dh)
     assert lm.lmce_read_status(ws) == _lib.LMCE_ERR_LABEL
     assert math.isnan(float(loss_bad)) and math.isfinite(float(loss))
     assert torch.isfinite(dh).all() and torch.isfinite(dW).all()
