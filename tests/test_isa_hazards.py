@@ -33,7 +33,9 @@ import pytest
 
 from lm_head_chunked_amd import build
 
-LGKM_OPS = ("ds_", "s_load", "s_buffer_load", "s_memtime", "s_memrealtime", "s_sendmsg", "s_getreg")
+# Scalar-memory operations: counted by lgkmcnt like LDS operations, but their
+# results return out of order.
+SMEM_OPS = ("s_load", "s_buffer_load", "s_memtime", "s_memrealtime", "s_dcache", "s_scratch_load", "s_atc_probe")
 WIDE_STORE = re.compile(r"^(buffer|global|scratch|flat)_store_(dwordx3|dwordx4|b96|b128)\b")
 
 
@@ -77,10 +79,14 @@ def kernel_programs(asm):
 def inflight_problems(insts, labels, depth=16):
     """Instructions that touch a register of an inline-asm LDS read still in flight, on any path.
 
-    A path state is (instruction index, queue of outstanding LGKM operations),
+    A path state is (instruction index, queue of outstanding LDS operations),
     where an inline-asm ds_read carries its destination registers and any other
-    LGKM operation none; s_waitcnt lgkmcnt(n) keeps the newest n (LDS reads
-    complete in order, and other LGKM operations only make a wait later)."""
+    LDS operation none; s_waitcnt lgkmcnt(n) keeps the newest n.  LDS
+    operations complete in order.  Scalar-memory operations (s_load,
+    s_memtime, ...) also count in lgkmcnt but complete out of order, so they
+    are not queued: with one outstanding, lgkmcnt(n) may be met while the
+    newest n LDS operations are still in flight, which is what keeping the
+    newest n LDS entries models."""
     problems, seen, work = set(), set(), [(0, ())]
     while work:
         i, q = work.pop()
@@ -103,7 +109,7 @@ def inflight_problems(insts, labels, depth=16):
             else:
                 if regs_va(args) & live:
                     problems.add(f"'{s}' touches {sorted(regs_va(args) & live)[:4]} while a fragment read is in flight")
-                if op.startswith(LGKM_OPS):
+                if op.startswith("ds_"):
                     q = q + ((),)
             q = q[-depth:]
             if op == "s_endpgm":
@@ -172,7 +178,7 @@ def device_asm():
         pytest.skip("hipcc not available")
     texts = {}
     with tempfile.TemporaryDirectory() as tmp:
-        for src in ("lmce_fwd.hip", "lmce_bwd.hip"):
+        for src in ("lmce_fwd.hip", "lmce_bwd.hip", "lmce_gemm.hip"):
             out = os.path.join(tmp, src + ".s")
             cmd = [build.hipcc(), *[f for f in build.flags() if f != "-fPIC"], "--cuda-device-only", "-S",
                    os.path.join(build.CSRC, src), "-o", out]
@@ -216,7 +222,7 @@ def test_fragment_reads_in_flight_are_left_alone(device_asm):
             problems, states = inflight_problems(insts, labels)
             assert states > len(insts) // 2, kern
             assert not problems, kern + ":\n" + "\n".join(sorted(problems)[:10])
-    assert kernels >= 6  # the group passes and the plain forward use the engine
+    assert kernels >= 10  # the group passes, the plain forward and the GEMM kernels use the engine
 
 
 def test_inflight_checker_follows_the_back_edge():
@@ -244,3 +250,27 @@ def test_inflight_checker_follows_the_back_edge():
     insts[1] = ("v_add_u32_e32 v5, 1, v5", False)  # now the loop top reuses a register of the read
     problems, _ = inflight_problems(insts, labels)
     assert len(problems) == 1 and "v5" in next(iter(problems))
+
+
+def test_inflight_checker_treats_scalar_loads_as_out_of_order():
+    """The scanner itself: an s_memtime issued after a fragment read does not
+    let lgkmcnt(1) retire that read (the scalar result may have come back
+    first), so touching the read's registers after that wait is a problem;
+    after lgkmcnt(0) it is not."""
+    body = [
+        "_Zkernel:",
+        "\t;;#ASMSTART",
+        "\tds_read_b128 v[4:7], v9",
+        "\t;;#ASMEND",
+        "\ts_memtime s[2:3]",
+        "\ts_waitcnt lgkmcnt(1)",
+        "\tv_mov_b32_e32 v5, v1",
+        "\ts_endpgm",
+    ]
+    insts, labels = kernel_programs("\n".join(body))["_Zkernel"]
+    problems, _ = inflight_problems(insts, labels)
+    assert len(problems) == 1 and "v5" in next(iter(problems))
+    body[5] = "\ts_waitcnt lgkmcnt(0)"
+    insts, labels = kernel_programs("\n".join(body))["_Zkernel"]
+    problems, _ = inflight_problems(insts, labels)
+    assert problems == set()
