@@ -9,10 +9,15 @@
  * rows at a time so that the L x V logits are never held whole; rows split
  * cleanly because each row's softmax runs over its own vocabulary only.
  *
- * This library goes further than row chunks: no logits block is ever written
- * to memory.  Each logit tile exists only in registers while a kernel folds
- * it into a running per-row log-sum-exp (forward) or into the gradient
- * contractions (backward).
+ * This library goes further than row chunks: no array of logits is ever
+ * allocated or written whole.  In the plain forward each fp32 logit tile
+ * exists only in registers while a kernel folds it into a running per-row
+ * log-sum-exp.  The group-scheduled passes (the backward, and the training
+ * forward) turn each tile into bf16 probabilities or G in registers and hand
+ * it to the other workgroups of their group through a fixed exchange ring in
+ * the workspace (at most 64 MiB), where it lives for the one round that
+ * consumes it: over a pass every logit crosses that ring once as 2 bytes,
+ * L x V x 2 bytes in all, but never more than the ring at a time.
  *
  *   lse_i  = log sum_v exp(z_iv)                       every row i
  *   loss   = sum_{i : y_i != ignore_index} (lse_i - z_{i,y_i}) / N
