@@ -21,11 +21,15 @@ namespace lmce {
 constexpr int kGemmThreads = 512;
 constexpr uint32_t kDrop = 0xfffffff0u;  // a buffer offset past every resource end: the access is dropped
 
-// Tile (tm, tn) of workgroup b: patches of patch_m x (32 / patch_m) tiles,
-// patch p of every 8 consecutive ones on XCD p % 8 (workgroups are dispatched
-// to the XCDs round-robin); patch_m == 0: row-major order (for grids with
-// fewer tiles than CUs, which patches would crowd onto a few XCDs).  False
-// for the padding workgroups of the grid.
+// Tile (tm, tn) of workgroup b.  patch_m > 0: the tiles are ordered
+// patch-major (patches of patch_m x (32 / patch_m) tiles, row-major over the
+// patches and within each patch; a partial patch at the grid's edge keeps
+// only its tiles inside the grid), and XCD x (workgroups are dispatched to
+// the 8 XCDs round-robin, so b % 8 is the XCD) takes the x-th of eight equal
+// consecutive shares of that order.  The 32 workgroups an XCD runs at once
+// then cover a compact block of tiles that share operand rows in its L2, and
+// every XCD gets the same number of tiles.  patch_m == 0: row-major order
+// (for grids with fewer tiles than CUs).  False for the grid's padding.
 __device__ __forceinline__ bool gemm_tile(int b, const GemmArgs& p, int& tm, int& tn) {
   const int mt = (int)((p.M + 255) / 256), nt = (int)((p.N + 255) / 256);
   if (p.patch_m == 0) {
@@ -33,13 +37,22 @@ __device__ __forceinline__ bool gemm_tile(int b, const GemmArgs& p, int& tm, int
     tn = b % nt;
     return tm < mt;
   }
+  const int total = mt * nt;
+  const int share = (total + 7) / 8;
+  const int t = (b & 7) * share + (b >> 3);  // position in the patch-major order
+  if ((b >> 3) >= share || t >= total) return false;
   const int pm = p.patch_m, pn = 32 / pm;
-  const int x = b & 7, j = b >> 3;
-  const int patch = (j >> 5) * 8 + x, w = j & 31;
-  const int npn = (nt + pn - 1) / pn;
-  tm = (patch / npn) * pm + w / pn;
-  tn = (patch % npn) * pn + w % pn;
-  return tm < mt && tn < nt;
+  // patches of full height come first in each band of pm tile rows; the
+  // band's width is nt, its last patch may be narrower
+  const int band = t / (pm * nt);             // band of pm tile rows
+  const int rows = min(pm, mt - band * pm);   // tile rows in this band
+  const int in_band = t - band * pm * nt;
+  const int patch = in_band / (rows * pn);    // full-width patches of this band
+  const int pw = min(pn, nt - patch * pn);    // width of this patch
+  const int w = in_band - patch * rows * pn;  // position in the patch
+  tm = band * pm + w / pw;
+  tn = patch * pn + w % pw;
+  return true;
 }
 
 // Operand of the tile whose first row is r0, for the K piece starting at k0.
@@ -205,11 +218,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0 || a.ksplit <= 0) return hipSuccess;
   const int64_t mt = (a.M + 255) / 256, nt = (a.N + 255) / 256;
   int64_t blocks = mt * nt;
-  if (a.patch_m > 0) {
-    const int pm = a.patch_m, pn = 32 / pm;
-    int64_t patches = ((mt + pm - 1) / pm) * ((nt + pn - 1) / pn);
-    blocks = (patches + 7) / 8 * 8 * 32;
-  }
+  if (a.patch_m > 0) blocks = (blocks + 7) / 8 * 8;  // eight equal shares, one per XCD
   const dim3 grid((unsigned)blocks, (unsigned)a.ksplit);
   if (a.a_tiled && a.b_tiled) hipLaunchKernelGGL((k_gemm<1, 1>), grid, dim3(kGemmThreads), 0, st, a);
   else if (a.a_tiled) hipLaunchKernelGGL((k_gemm<1, 0>), grid, dim3(kGemmThreads), 0, st, a);
