@@ -87,6 +87,9 @@ __device__ __forceinline__ float load_bf16(rsrc_t rs, uint32_t off) {
 __device__ __forceinline__ void store_bf16(rsrc_t rs, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), rs, off, 0, 0);
 }
+__device__ __forceinline__ void store_b64(rsrc_t rs, uint32_t off, uint64_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, 0);
+}
 
 // Accumulator element (mb, nb, reg) of lane `lane` in wave (wm, wn) sits at
 // tile row wm*64 + mb*32 + acc_row(reg, lane), tile column wn*128 + nb*32 + lane%32.
@@ -116,17 +119,26 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     float* base = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.c_split + m0 * p.ldc + n0;
     const rsrc_t rs = make_rsrc(base, (uint64_t)((int64_t)(rl - 1) * ldc + cl) * 4);
     const bool accum = p.epi == kEpiAccF32;
+    // The accumulate loads the 16 old values of a 32x32 block before its
+    // first store: a load may not pass an earlier store to a possibly equal
+    // address, so interleaved load-add-store pairs would wait for one L2
+    // round trip each.
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int reg = 0; reg < 16; ++reg) {
-        const int r = wm * 64 + mb * 32 + acc_row(reg, lane);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int c = wn * 128 + nb * 32 + (lane & 31);
+        float old[16];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int c = wn * 128 + nb * 32 + (lane & 31);
+        for (int reg = 0; reg < 16; ++reg) {
+          const int r = wm * 64 + mb * 32 + acc_row(reg, lane);
+          old[reg] = accum ? load_f32(rs, (r < rl && c < cl) ? (uint32_t)(r * ldc + c) * 4u : kDrop) : 0.f;
+        }
+#pragma unroll
+        for (int reg = 0; reg < 16; ++reg) {
+          const int r = wm * 64 + mb * 32 + acc_row(reg, lane);
           const uint32_t off = (r < rl && c < cl) ? (uint32_t)(r * ldc + c) * 4u : kDrop;
-          const float v = alpha * acc[mb][nb][reg];
-          store_f32(rs, off, accum ? load_f32(rs, off) + v : v);
+          store_f32(rs, off, old[reg] + alpha * acc[mb][nb][reg]);
         }
       }
   } else if (p.epi == kEpiStoreBf16) {
@@ -163,36 +175,62 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
         }
       }
   } else if (p.epi == kEpiSwigluBwd) {
-    // acc = d(act) at unit i = column; gate/up of unit i at 64 (i / 32) + i % 32 (+ 32)
+    // acc = d(act) at unit i = column; gate/up of unit i at 64 (i / 32) + i % 32 (+ 32) of the
+    // row.  Outputs: d(gate/up) row-major at C (the dx GEMM's A operand), and K-tiled
+    // transposes of d(gate/up) at gT and of silu(g) * u at aux (the weight-gradient GEMMs'
+    // operands over the chunk's rows, [t_rows / 128][columns][128]): the lane's registers
+    // 4q .. 4q + 3 are four consecutive rows of one column, i.e. 8 contiguous bytes there.
+    // Rows from M up to t_rows come out as zeros (their acc and gate/up values read as 0).
     const int64_t n2 = 2 * p.N;
-    const rsrc_t rgu = make_rsrc(p.gu + m0 * n2, (uint64_t)((int64_t)(rl - 1) * n2 + n2) * 2);
-    const rsrc_t rdg = make_rsrc(static_cast<uint16_t*>(p.C) + m0 * n2, (uint64_t)((int64_t)(rl - 1) * n2 + n2) * 2);
-    const int la = (int)p.ld_aux;
-    const rsrc_t rac = make_rsrc(p.aux + m0 * p.ld_aux, (uint64_t)((int64_t)(rl - 1) * la + p.N) * 2);
+    const int tl = (int)min<int64_t>(256, p.t_rows - m0);  // rows of this tile in the K-tiled outputs
+    const rsrc_t rgu = make_rsrc(p.gu + m0 * n2, (uint64_t)rl * n2 * 2);
+    const rsrc_t rdg = make_rsrc(static_cast<uint16_t*>(p.C) + m0 * n2, (uint64_t)rl * n2 * 2);
+    const rsrc_t rgT = make_rsrc(p.gT + (m0 / 128) * n2 * 128, (uint64_t)((tl + 127) / 128) * n2 * 128 * 2);
+    const rsrc_t raT = make_rsrc(p.aux + (m0 / 128) * p.N * 128, (uint64_t)((tl + 127) / 128) * p.N * 128 * 2);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int reg = 0; reg < 16; ++reg) {
-        const int r = wm * 64 + mb * 32 + acc_row(reg, lane);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int64_t i = n0 + wn * 128 + nb * 32 + (lane & 31);
+        const uint32_t gcol = (uint32_t)((i >> 5) * 64 + (i & 31));
+        float g[16], u[16];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int64_t i = n0 + wn * 128 + nb * 32 + (lane & 31);
-          const bool in = r < rl && i < p.N;
-          const uint32_t gcol = (uint32_t)((i >> 5) * 64 + (i & 31));
-          const uint32_t og = in ? ((uint32_t)r * (uint32_t)n2 + gcol) * 2u : kDrop;
-          const uint32_t ou = in ? og + 64u : kDrop;
-          const float g = load_bf16(rgu, og), u = load_bf16(rgu, ou);
-          const float d = alpha * acc[mb][nb][reg];
-          const float sg = 1.f / (1.f + exp2_fast(-g * kLog2e));
-          const float silu = g * sg;
-          store_bf16(rdg, og, d * u * sg * (1.f + g * (1.f - sg)));
-          store_bf16(rdg, ou, d * silu);
-          store_bf16(rac, in ? (uint32_t)(r * la + i) * 2u : kDrop, silu * u);
+        for (int reg = 0; reg < 16; ++reg) {  // every load of the block first
+          const int r = wm * 64 + mb * 32 + acc_row(reg, lane);
+          const uint32_t og = (r < rl && i < p.N) ? ((uint32_t)r * (uint32_t)n2 + gcol) * 2u : kDrop;
+          g[reg] = load_bf16(rgu, og);
+          u[reg] = load_bf16(rgu, og == kDrop ? kDrop : og + 64u);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float dg[4], du[4], pa[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int reg = 4 * q + e;
+            const float d = alpha * acc[mb][nb][reg];
+            const float sg = 1.f / (1.f + exp2_fast(-g[reg] * kLog2e));
+            const float silu = g[reg] * sg;
+            dg[e] = d * u[reg] * sg * (1.f + g[reg] * (1.f - sg));
+            du[e] = d * silu;
+            pa[e] = silu * u[reg];
+            const int r = wm * 64 + mb * 32 + acc_row(reg, lane);
+            const uint32_t og = (r < rl && i < p.N) ? ((uint32_t)r * (uint32_t)n2 + gcol) * 2u : kDrop;
+            store_bf16(rdg, og, dg[e]);
+            store_bf16(rdg, og == kDrop ? kDrop : og + 64u, du[e]);
+          }
+          const int r4 = wm * 64 + mb * 32 + acc_row(4 * q, lane);  // first of the four rows
+          const bool tin = r4 < tl && i < p.N;
+          const uint32_t blk = (uint32_t)(r4 >> 7), within = (uint32_t)(r4 & 127);
+          const uint32_t ogT = tin ? ((blk * (uint32_t)n2 + gcol) * 128u + within) * 2u : kDrop;
+          const uint32_t oaT = tin ? ((blk * (uint32_t)p.N + (uint32_t)i) * 128u + within) * 2u : kDrop;
+          store_b64(rgT, ogT, pack_bf16x4(dg[0], dg[1], dg[2], dg[3]));
+          store_b64(rgT, tin ? ogT + 32u * 128u * 2u : kDrop, pack_bf16x4(du[0], du[1], du[2], du[3]));
+          store_b64(raT, oaT, pack_bf16x4(pa[0], pa[1], pa[2], pa[3]));
         }
       }
   } else if (p.epi == kEpiAccF32Gu) {
     // tile rows wm*64 + [0, 32) are gate rows, wm*64 + [32, 64) up rows, of
-    // units (m0 + wm*64)/2 + [0, 32)
+    // units (m0 + wm*64)/2 + [0, 32); old values loaded before any store, as above
     const int64_t units = p.M / 2;
     const int64_t u0 = m0 / 2;
     const int ul = (int)min<int64_t>(128, units - u0);
@@ -201,13 +239,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
       float* base = static_cast<float*>(mb == 0 ? p.C : p.C2) + u0 * p.ldc + n0;
       const rsrc_t rs = make_rsrc(base, (uint64_t)((int64_t)(ul - 1) * ldc + cl) * 4);
 #pragma unroll
-      for (int reg = 0; reg < 16; ++reg) {
-        const int ur = wm * 32 + acc_row(reg, lane);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int c = wn * 128 + nb * 32 + (lane & 31);
+        float old[16];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int c = wn * 128 + nb * 32 + (lane & 31);
+        for (int reg = 0; reg < 16; ++reg) {
+          const int ur = wm * 32 + acc_row(reg, lane);
+          old[reg] = load_f32(rs, (ur < ul && c < cl) ? (uint32_t)(ur * ldc + c) * 4u : kDrop);
+        }
+#pragma unroll
+        for (int reg = 0; reg < 16; ++reg) {
+          const int ur = wm * 32 + acc_row(reg, lane);
           const uint32_t off = (ur < ul && c < cl) ? (uint32_t)(ur * ldc + c) * 4u : kDrop;
-          store_f32(rs, off, load_f32(rs, off) + alpha * acc[mb][nb][reg]);
+          store_f32(rs, off, old[reg] + alpha * acc[mb][nb][reg]);
         }
       }
     }

@@ -116,7 +116,8 @@ enum GemmEpi {
   kEpiStoreBf16 = 2,  // C bf16 [M][ldc] = alpha * acc
   kEpiSwigluFwd = 3,  // acc = gate/up pairs (32-column blocks interleaved): C bf16 [M][ldc] = silu(g) * u at column i
   kEpiSwigluBwd = 4,  // acc = d(act) [M][N]: reads gate/up gu bf16 [M][2N] (interleaved); C bf16 [M][2N] = d(gate/up)
-                      // interleaved, aux bf16 [M][N] = silu(g) * u
+                      // interleaved, and K-tiled transposes [t_rows / 128][cols][128] of it (gT) and of
+                      // silu(g) * u (aux), zero for rows M .. t_rows
   kEpiAccF32Gu = 5,   // C (gate rows) and C2 (up rows) fp32 [M/2][ldc] += alpha * acc, A rows interleaved
 };
 
@@ -138,8 +139,9 @@ struct GemmArgs {
   void* C2;
   int64_t ldc, c_split;
   const uint16_t* gu;   // kEpiSwigluBwd: gate/up values
-  uint16_t* aux;        // kEpiSwigluBwd: act output
-  int64_t ld_aux;
+  uint16_t* gT;         // kEpiSwigluBwd: K-tiled d(gate/up)
+  uint16_t* aux;        // kEpiSwigluBwd: K-tiled silu(g) * u
+  int64_t t_rows;       // kEpiSwigluBwd: rows of the K-tiled outputs (a multiple of 128, >= M)
   int patch_m;          // tile order: patches of patch_m (1, 2, 4, 8) x (32 / patch_m) tiles, one patch per XCD
                         // at a time; 0: row-major
 };

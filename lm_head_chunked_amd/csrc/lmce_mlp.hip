@@ -20,7 +20,8 @@
 //                        y_c = p_c Wd^T                      (GEMM, fp32 out)
 // Backward, per chunk c (upstream dy):
 //   gu_c = x_c [Wg; Wu]^T            recomputed (GEMM, bf16)
-//   dp_c = dy_c Wd, and in the same epilogue dg_c, du_c (bf16) and p_c (bf16)
+//   dp_c = dy_c Wd, and in the same epilogue dg_c, du_c (bf16, row-major and K-tiled
+//          transposed) and p_c (bf16, K-tiled transposed)
 //   dx_c = dg_c Wg + du_c Wu          (one GEMM over the packed 2I)
 //   dWd += dy_c^T p_c, dWg += dg_c^T x_c, dWu += du_c^T x_c   (GEMMs, K = the chunk's rows)
 
@@ -230,7 +231,6 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     return LMCE_ERR_HIP;
   const uint16_t* Wgu = at<uint16_t>(workspace, p.off_Wgu);
   uint16_t* gu = at<uint16_t>(workspace, p.off_gu);
-  uint16_t* act = at<uint16_t>(workspace, p.off_act);
   uint16_t* dgu = at<uint16_t>(workspace, p.off_dgu);
   uint16_t* actT = at<uint16_t>(workspace, p.off_actT);
   uint16_t* dguT = at<uint16_t>(workspace, p.off_dguT);
@@ -254,8 +254,9 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     d.alpha = 1.f;
     d.C = dgu;
     d.gu = gu;
-    d.aux = act;
-    d.ld_aux = I;
+    d.gT = dguT;
+    d.aux = actT;
+    d.t_rows = rp;
     d.patch_m = 4;
     if (launch_gemm(d, s) != hipSuccess) return LMCE_ERR_HIP;
     // dx_c = [dg | du] [Wg; Wu] (B = the packed matrix transposed, K = 2I)
@@ -272,10 +273,9 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     xg.ldc = H;
     xg.patch_m = 4;
     if (launch_gemm(xg, s) != hipSuccess) return LMCE_ERR_HIP;
-    // weight gradients: K = the chunk's rows, from K-tiled transposes (zero past `rows`)
-    if (launch_transpose(act, rows, I, actT, rp, s) != hipSuccess ||
-        launch_transpose(dgu, rows, 2 * I, dguT, rp, s) != hipSuccess ||
-        launch_transpose(dy16 + r0 * H, rows, H, dyT, rp, s) != hipSuccess ||
+    // weight gradients: K = the chunk's rows, from K-tiled transposes (zero past `rows`):
+    // those of p and [dg | du] came out of the dp GEMM's epilogue
+    if (launch_transpose(dy16 + r0 * H, rows, H, dyT, rp, s) != hipSuccess ||
         launch_transpose(x16 + r0 * H, rows, H, xT, rp, s) != hipSuccess)
       return LMCE_ERR_HIP;
     GemmArgs wd = {};
