@@ -90,6 +90,30 @@ __device__ __forceinline__ void store_bf16(rsrc_t rs, uint32_t off, float v) {
 __device__ __forceinline__ void store_b64(rsrc_t rs, uint32_t off, uint64_t v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, 0);
 }
+// 16-byte accesses; the scalar offset stays the constant 0 (see store_sc1_b128)
+__device__ __forceinline__ void store_b128(rsrc_t rs, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 load_b128(rsrc_t rs, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+}
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// alpha * registers base .. base + 7 of an accumulator block as 8 bf16 (round to nearest even)
+__device__ __forceinline__ u32x4 pack_bf16x8(const f32x16& v, int base, float alpha) {
+  const f32x8 t = {alpha * v[base + 0], alpha * v[base + 1], alpha * v[base + 2], alpha * v[base + 3],
+                   alpha * v[base + 4], alpha * v[base + 5], alpha * v[base + 6], alpha * v[base + 7]};
+  return __builtin_bit_cast(u32x4, __builtin_convertvector(t, bf16x8));
+}
+
+// Register `reg` (0 .. 15) of a fragment-order block held as two 16-byte words.
+__device__ __forceinline__ float frag_bf16(const u32x4 (&w)[2], int reg) {
+  const uint32_t x = w[reg >> 3][(reg & 7) >> 1];
+  return __builtin_bit_cast(float, (reg & 1) ? (x & 0xffff0000u) : (x << 16));
+}
 
 // Accumulator element (mb, nb, reg) of lane `lane` in wave (wm, wn) sits at
 // tile row wm*64 + mb*32 + acc_row(reg, lane), tile column wn*128 + nb*32 + lane%32.
@@ -141,19 +165,18 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
           store_f32(rs, off, old[reg] + alpha * acc[mb][nb][reg]);
         }
       }
-  } else if (p.epi == kEpiStoreBf16) {
-    uint16_t* base = static_cast<uint16_t*>(p.C) + (int64_t)blockIdx.y * p.c_split + m0 * p.ldc + n0;
-    const rsrc_t rs = make_rsrc(base, (uint64_t)((int64_t)(rl - 1) * ldc + cl) * 2);
+  } else if (p.epi == kEpiStoreFrag) {
+    // each lane's 16 registers of a 32 x 32 block as 32 contiguous bytes: a
+    // consumer with the same tile and lane layout reads them back whole
+    const int64_t ntn = (p.N + 255) / 256;
+    const rsrc_t rs = make_rsrc(static_cast<uint16_t*>(p.C) + ((int64_t)tm * ntn + tn) * 65536, 131072);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int reg = 0; reg < 16; ++reg) {
-        const int r = wm * 64 + mb * 32 + acc_row(reg, lane);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int c = wn * 128 + nb * 32 + (lane & 31);
-          store_bf16(rs, (r < rl && c < cl) ? (uint32_t)(r * ldc + c) * 2u : kDrop, alpha * acc[mb][nb][reg]);
-        }
+      for (int nb = 0; nb < 4; ++nb) {
+        const uint32_t off = ((uint32_t)(wave * 8 + mb * 4 + nb) * 1024u + (uint32_t)lane * 16u) * 2u;
+        store_b128(rs, off, pack_bf16x8(acc[mb][nb], 0, alpha));
+        store_b128(rs, off + 16u, pack_bf16x8(acc[mb][nb], 8, alpha));
       }
   } else if (p.epi == kEpiSwigluFwd) {
     // tile columns 64q + j (gate) and 64q + 32 + j (up) are unit i = 32q + j
@@ -175,59 +198,115 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
         }
       }
   } else if (p.epi == kEpiSwigluBwd) {
-    // acc = d(act) at unit i = column; gate/up of unit i at 64 (i / 32) + i % 32 (+ 32) of the
-    // row.  Outputs: d(gate/up) row-major at C (the dx GEMM's A operand), and K-tiled
-    // transposes of d(gate/up) at gT and of silu(g) * u at aux (the weight-gradient GEMMs'
-    // operands over the chunk's rows, [t_rows / 128][columns][128]): the lane's registers
-    // 4q .. 4q + 3 are four consecutive rows of one column, i.e. 8 contiguous bytes there.
-    // Rows from M up to t_rows come out as zeros (their acc and gate/up values read as 0).
+    // acc = d(act) at unit i = column.  The gate and up values of unit i sit at columns
+    // 64 (i / 32) + i % 32 and + 32 of the gate/up GEMM, which stored them in fragment order:
+    // this lane's are in that GEMM's tile (tm, 2 tn + wn), wave 2 wm + nb / 2, blocks
+    // mb * 4 + 2 (nb % 2) (gate) and + 1 (up), at the same lane and registers.
+    // Outputs, staged through LDS one 32-unit column block nb at a time (64 units of the tile):
+    //  * d(gate/up) row-major at C, interleaved like the gate/up columns (the dx GEMM's A),
+    //  * K-tiled transposes [t_rows / 128][columns][128] of d(gate/up) at gT and of
+    //    silu(g) * u at aux (the weight-gradient GEMMs' operands over the chunk's rows).
+    // Rows from M up to t_rows come out as zeros (their acc and gate/up values are 0).
+    // LDS holds 192 columns (d(gate), d(up) of the two wave columns, then p) of 256 rows, in
+    // 8-byte units of four rows: unit (col, rq) at col * 64 + (rq ^ 2 (col % 16)), so that the
+    // lanes' 8-byte writes, the 16-byte column reads and the transposing reads below spread
+    // over the banks.
     const int64_t n2 = 2 * p.N;
+    const int64_t ntg = (n2 + 255) / 256;  // tiles per tile row of the gate/up GEMM
     const int tl = (int)min<int64_t>(256, p.t_rows - m0);  // rows of this tile in the K-tiled outputs
-    const rsrc_t rgu = make_rsrc(p.gu + m0 * n2, (uint64_t)rl * n2 * 2);
+    const int64_t gtile = 2 * (int64_t)tn + wn;
+    const rsrc_t rgu = make_rsrc(p.gu + ((int64_t)tm * ntg + gtile) * 65536, gtile < ntg ? 131072 : 0);
     const rsrc_t rdg = make_rsrc(static_cast<uint16_t*>(p.C) + m0 * n2, (uint64_t)rl * n2 * 2);
     const rsrc_t rgT = make_rsrc(p.gT + (m0 / 128) * n2 * 128, (uint64_t)((tl + 127) / 128) * n2 * 128 * 2);
     const rsrc_t raT = make_rsrc(p.aux + (m0 / 128) * p.N * 128, (uint64_t)((tl + 127) / 128) * p.N * 128 * 2);
+    uint64_t* st = reinterpret_cast<uint64_t*>(lds);
+    auto unit = [](int col, int rq) { return col * 64 + (rq ^ (2 * (col & 15))); };
+    // [mb][0..1] gate registers 0..7, 8..15; [mb][2..3] up
+    u32x4 gu[2][2][4];
+    auto load_gu = [&](int nb, u32x4 (&d)[2][4]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        const uint32_t off = ((uint32_t)((wm * 2 + (nb >> 1)) * 8 + mb * 4 + 2 * (nb & 1)) * 1024u +
+                              (uint32_t)lane * 16u) * 2u;
+        d[mb][0] = load_b128(rgu, off);
+        d[mb][1] = load_b128(rgu, off + 16u);
+        d[mb][2] = load_b128(rgu, off + 2048u);
+        d[mb][3] = load_b128(rgu, off + 2064u);
+      }
+    };
+    load_gu(0, gu[0]);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int64_t i = n0 + wn * 128 + nb * 32 + (lane & 31);
-        const uint32_t gcol = (uint32_t)((i >> 5) * 64 + (i & 31));
-        float g[16], u[16];
+    for (int nb = 0; nb < 4; ++nb) {
+      u32x4 (&cur)[2][4] = gu[nb & 1];
+      // every wave is past its last read of the LDS (the GEMM's stages, or the previous block)
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      raw_barrier();
 #pragma unroll
-        for (int reg = 0; reg < 16; ++reg) {  // every load of the block first
-          const int r = wm * 64 + mb * 32 + acc_row(reg, lane);
-          const uint32_t og = (r < rl && i < p.N) ? ((uint32_t)r * (uint32_t)n2 + gcol) * 2u : kDrop;
-          g[reg] = load_bf16(rgu, og);
-          u[reg] = load_bf16(rgu, og == kDrop ? kDrop : og + 64u);
-        }
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4 gw[2] = {cur[mb][0], cur[mb][1]}, uw[2] = {cur[mb][2], cur[mb][3]};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float dg[4], du[4], pa[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int reg = 4 * q + e;
+            const float g = frag_bf16(gw, reg), u = frag_bf16(uw, reg);
             const float d = alpha * acc[mb][nb][reg];
-            const float sg = 1.f / (1.f + exp2_fast(-g[reg] * kLog2e));
-            const float silu = g[reg] * sg;
-            dg[e] = d * u[reg] * sg * (1.f + g[reg] * (1.f - sg));
+            const float sg = 1.f / (1.f + exp2_fast(-g * kLog2e));
+            const float silu = g * sg;
+            dg[e] = d * u * sg * (1.f + g * (1.f - sg));
             du[e] = d * silu;
-            pa[e] = silu * u[reg];
-            const int r = wm * 64 + mb * 32 + acc_row(reg, lane);
-            const uint32_t og = (r < rl && i < p.N) ? ((uint32_t)r * (uint32_t)n2 + gcol) * 2u : kDrop;
-            store_bf16(rdg, og, dg[e]);
-            store_bf16(rdg, og == kDrop ? kDrop : og + 64u, du[e]);
+            pa[e] = silu * u;
           }
-          const int r4 = wm * 64 + mb * 32 + acc_row(4 * q, lane);  // first of the four rows
-          const bool tin = r4 < tl && i < p.N;
-          const uint32_t blk = (uint32_t)(r4 >> 7), within = (uint32_t)(r4 & 127);
-          const uint32_t ogT = tin ? ((blk * (uint32_t)n2 + gcol) * 128u + within) * 2u : kDrop;
-          const uint32_t oaT = tin ? ((blk * (uint32_t)p.N + (uint32_t)i) * 128u + within) * 2u : kDrop;
-          store_b64(rgT, ogT, pack_bf16x4(dg[0], dg[1], dg[2], dg[3]));
-          store_b64(rgT, tin ? ogT + 32u * 128u * 2u : kDrop, pack_bf16x4(du[0], du[1], du[2], du[3]));
-          store_b64(raT, oaT, pack_bf16x4(pa[0], pa[1], pa[2], pa[3]));
+          const int rq = wm * 16 + mb * 8 + 2 * q + (lane >> 5);  // rows 4 rq .. 4 rq + 3
+          const int c = lane & 31;
+          st[unit(wn * 64 + c, rq)] = pack_bf16x4(dg[0], dg[1], dg[2], dg[3]);
+          st[unit(wn * 64 + 32 + c, rq)] = pack_bf16x4(du[0], du[1], du[2], du[3]);
+          st[unit(128 + wn * 32 + c, rq)] = pack_bf16x4(pa[0], pa[1], pa[2], pa[3]);
         }
       }
+      if (nb + 1 < 4) load_gu(nb + 1, gu[(nb + 1) & 1]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      raw_barrier();
+      // K-tiled transposes: 16 lanes move one column's 128-row block (256 contiguous bytes)
+#pragma unroll
+      for (int s = 0; s < 12; ++s) {
+        const int w = s * kGemmThreads + (int)threadIdx.x;
+        const int col = w >> 5, blk = (w >> 4) & 1, ch = w & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + unit(col, blk * 32 + 2 * ch));
+        const bool rows_in = blk * 128 < tl;
+        if (s < 8) {  // columns 0 .. 127: d(gate/up)
+          const int64_t gcol = 512 * (int64_t)tn + 256 * (col >> 6) + 64 * nb + (col & 63);
+          store_b128(rgT, (rows_in && gcol < n2) ? (uint32_t)(((blk * n2 + gcol) * 128 + ch * 8) * 2) : kDrop, v);
+        } else {      // columns 128 .. 191: p
+          const int a = col - 128;
+          const int64_t i = 256 * (int64_t)tn + 128 * (a >> 5) + 32 * nb + (a & 31);
+          store_b128(raT, (rows_in && i < p.N) ? (uint32_t)(((blk * p.N + i) * 128 + ch * 8) * 2) : kDrop, v);
+        }
+      }
+      // row-major d(gate/up): transposing reads (ds_read_b64_tr_b16).  In a group of 16 lanes,
+      // lane k reads rows 4 (rq0 + k % 4) .. + 3 of column c0 + k / 4; lane i then holds
+      // columns c0 .. c0 + 3 of row 4 rq0 + i.  Group g of the wave takes columns
+      // 32 cb + 8 g .. + 7 (two reads), so that each row gets 64 contiguous bytes.
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int t = s * 8 + wave;
+        const int rb = t & 15, cb = t >> 4;
+        const int k = lane & 15, g = lane >> 4;
+        const int c0 = 32 * cb + 8 * g + (k >> 2);
+        const int rq = 4 * rb + (k & 3);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(st + unit(c0, rq)));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(st + unit(c0 + 4, rq)));
+        const int r = 16 * rb + k;
+        const int cc = 32 * cb + 8 * g;
+        const int64_t gcol = 512 * (int64_t)tn + 256 * (cc >> 6) + 64 * nb + (cc & 63);
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 v = {l2[0], l2[1], h2[0], h2[1]};
+        store_b128(rdg, (r < rl && gcol < n2) ? (uint32_t)((r * n2 + gcol) * 2) : kDrop, v);
+      }
+    }
   } else if (p.epi == kEpiAccF32Gu) {
     // tile rows wm*64 + [0, 32) are gate rows, wm*64 + [32, 64) up rows, of
     // units (m0 + wm*64)/2 + [0, 32); old values loaded before any store, as above

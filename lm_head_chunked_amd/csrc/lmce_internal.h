@@ -113,11 +113,12 @@ struct BwdArgs {
 enum GemmEpi {
   kEpiStoreF32 = 0,   // C fp32 [M][ldc] = alpha * acc
   kEpiAccF32 = 1,     // C fp32 [M][ldc] += alpha * acc
-  kEpiStoreBf16 = 2,  // C bf16 [M][ldc] = alpha * acc
+  kEpiStoreFrag = 2,  // C bf16 = alpha * acc in fragment order: per 256 x 256 tile (tm, tn), tile index
+                      // tm * ceil(N / 256) + tn, 64 blocks (wave, mb, nb) of 64 lanes x 16 accumulator registers
   kEpiSwigluFwd = 3,  // acc = gate/up pairs (32-column blocks interleaved): C bf16 [M][ldc] = silu(g) * u at column i
-  kEpiSwigluBwd = 4,  // acc = d(act) [M][N]: reads gate/up gu bf16 [M][2N] (interleaved); C bf16 [M][2N] = d(gate/up)
-                      // interleaved, and K-tiled transposes [t_rows / 128][cols][128] of it (gT) and of
-                      // silu(g) * u (aux), zero for rows M .. t_rows
+  kEpiSwigluBwd = 4,  // acc = d(act) [M][N]: reads the gate/up values gu [M][2N] (interleaved) in fragment order;
+                      // C bf16 [M][2N] = d(gate/up) interleaved, and K-tiled transposes [t_rows / 128][cols][128]
+                      // of it (gT) and of silu(g) * u (aux), zero for rows M .. t_rows
   kEpiAccF32Gu = 5,   // C (gate rows) and C2 (up rows) fp32 [M/2][ldc] += alpha * acc, A rows interleaved
 };
 

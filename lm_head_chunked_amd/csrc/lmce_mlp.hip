@@ -71,8 +71,8 @@ int mlp_plan(int64_t L, int64_t H, int64_t I, int64_t chunk_rows, MlpPlan* p) {
   off = up256(off + b * 2 * I * H);
   p->off_WdT = off;
   off = up256(off + b * H * I);
-  p->off_gu = off;
-  off = up256(off + b * p->cr * 2 * I);
+  p->off_gu = off;  // fragment order: whole 256 x 256 tiles
+  off = up256(off + b * ((p->cr + 255) / 256 * 256) * ((2 * I + 255) / 256 * 256));
   p->off_act = off;
   off = up256(off + b * p->cr * I);
   p->off_dgu = off;
@@ -126,7 +126,8 @@ void set_b_tiled(GemmArgs& g, const void* p, int64_t rows, int64_t kpad) {
 }
 
 // p_c = silu(g) * u of rows [r0, r0 + rows) into the act area; with
-// store_gu, the bf16 gate/up values themselves into the gu area instead.
+// store_gu, the bf16 gate/up values themselves into the gu area instead, in
+// the GEMM's fragment order.
 hipError_t gate_up(const MlpPlan& p, const void* x, const uint16_t* Wgu, int64_t r0, int64_t rows, void* ws,
                    bool store_gu, hipStream_t s) {
   GemmArgs g = {};
@@ -138,9 +139,8 @@ hipError_t gate_up(const MlpPlan& p, const void* x, const uint16_t* Wgu, int64_t
   g.ksplit = 1;
   g.alpha = 1.f;
   if (store_gu) {
-    g.epi = kEpiStoreBf16;
+    g.epi = kEpiStoreFrag;  // read back by the SwiGLU-backward epilogue, lane for lane
     g.C = at<uint16_t>(ws, p.off_gu);
-    g.ldc = 2 * p.I;
   } else {
     g.epi = kEpiSwigluFwd;
     g.C = at<uint16_t>(ws, p.off_act);
