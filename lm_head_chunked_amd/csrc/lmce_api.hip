@@ -35,9 +35,8 @@ int spin_limit() {
 struct Plan {
   int64_t L, H, V;
   int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
-  int64_t Lpad, Vpad;
   int hs, xbuf_wgs;
-  size_t off_pm, off_ps, off_bsum, off_hT, off_WT, off_sync, off_xbuf, off_park, off_xstat, off_cnt, off_crow,
+  size_t off_pm, off_ps, off_bsum, off_rows, off_sync, off_xbuf, off_park, off_xstat, off_cnt, off_crow,
       off_clab, off_clse, off_part, off_fperm, off_finv, total;
 };
 
@@ -70,8 +69,6 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->vtiles_per_seg = (p->vtiles + seg - 1) / seg;
   p->segments = (p->vtiles + p->vtiles_per_seg - 1) / p->vtiles_per_seg;
   p->xcd_map = (p->segments == 8 && p->ntiles % 32 == 0) ? 1 : 0;
-  p->Lpad = (L + 127) / 128 * 128;
-  p->Vpad = (V + 127) / 128 * 128;
   // Widest H slice of one backward workgroup.  A 256-wide slice parks its
   // accumulator (256 KiB out and back per round); the round's work grows with
   // H, so the move pays off only for wide hidden sizes.
@@ -84,10 +81,10 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   off = align256(off + sizeof(float) * (size_t)L * (size_t)p->segments);
   p->off_bsum = off;
   off = align256(off + sizeof(float) * (size_t)((L + 63) / 64));
-  p->off_hT = off;
-  off = align256(off + sizeof(uint16_t) * (size_t)H * (size_t)p->Lpad);
-  p->off_WT = off;
-  off = align256(off + sizeof(uint16_t) * (size_t)H * (size_t)p->Vpad);
+  // gathered h rows: the labelled-first rows of the training forward or of
+  // the dh pass, or the dW pass's compacted rows (one at a time)
+  p->off_rows = off;
+  off = align256(off + sizeof(uint16_t) * (size_t)H * (size_t)L);
   p->off_sync = off;
   off = align256(off + sizeof(unsigned) * (size_t)kMaxBwdWGs * kSyncStride);
   p->off_xbuf = off;
@@ -103,7 +100,7 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->off_xstat = off;
   off = align256(off + (size_t)wgs * kXstatPerWG);
   // dW pass on the labelled rows only: per-chunk counts, then their index,
-  // label and lse (their h rows go to the W^T area, free during that pass)
+  // label and lse (their h rows go to the rows area)
   p->off_cnt = off;
   off = align256(off + sizeof(int) * (size_t)((L + 1023) / 1024));
   p->off_crow = off;
@@ -117,7 +114,7 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->off_part = off;
   off = align256(off + (size_t)wgs * kParkPerWG);
   // training forward: labelled-first order of the rows and its inverse (the
-  // reordered h rows go to the h^T area, free during the forward)
+  // reordered h rows go to the rows area)
   p->off_fperm = off;
   off = align256(off + sizeof(int) * (size_t)L);
   p->off_finv = off;
@@ -169,7 +166,7 @@ namespace {
 
 // The plain forward on a prepared area: the header at `hdr` and the
 // per-segment partials and block sums at the plan's offsets from `base`
-// (the first p.off_hT bytes of a workspace layout).
+// (the first p.off_rows bytes of a workspace layout).
 int fwd_launch(const Plan& p, const void* h, const void* W, const int64_t* labels, int64_t ignore_index,
                float* loss_out, float* lse_out, void* base, hipStream_t s) {
   WsHeader* hdr = at<WsHeader>(base, 0);
@@ -261,7 +258,7 @@ extern "C" int lmce_fwd_noalloc(const void* h, const void* W, const int64_t* lab
   if (st != LMCE_OK) return st;
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(labels, 8) || !aligned(loss_out, 4) || !aligned(lse_out, 4))
     return LMCE_ERR_NULL;
-  if (L > kScratchMaxRows || p.off_hT > kScratchBytes) return LMCE_ERR_SCRATCH;  // the forward's part of the layout
+  if (L > kScratchMaxRows || p.off_rows > kScratchBytes) return LMCE_ERR_SCRATCH;  // the forward's part of the layout
   void* base = nullptr;
   st = scratch_on_current_device(&base);
   if (st != LMCE_OK) return st;
@@ -346,14 +343,10 @@ BwdArgs group_args(const Plan& p, const void* h, const void* W, const int64_t* l
   a.h = static_cast<const uint16_t*>(h);
   a.W = static_cast<const uint16_t*>(W);
   a.labels = labels;
-  a.hT = at<uint16_t>(workspace, p.off_hT);
-  a.WT = at<uint16_t>(workspace, p.off_WT);
   a.L = p.L;
   a.H = p.H;
   a.V = p.V;
   a.ignore_index = ignore_index;
-  a.Lpad = p.Lpad;
-  a.Vpad = p.Vpad;
   a.spin_limit = spin_limit();
   a.sync = at<unsigned>(workspace, p.off_sync);
   a.xbuf = at<uint16_t>(workspace, p.off_xbuf);
@@ -365,20 +358,19 @@ BwdArgs group_args(const Plan& p, const void* h, const void* W, const int64_t* l
   a.crow = at<int>(workspace, p.off_crow);
   a.clab = at<int64_t>(workspace, p.off_clab);
   a.clse = at<float>(workspace, p.off_clse);
-  a.ch = at<uint16_t>(workspace, p.off_WT);
+  a.ch = at<uint16_t>(workspace, p.off_rows);
   a.dw_part = at<float>(workspace, p.off_part);
   a.fperm = at<int>(workspace, p.off_fperm);
   a.finv = at<int>(workspace, p.off_finv);
-  a.hp = at<uint16_t>(workspace, p.off_hT);
+  a.hp = at<uint16_t>(workspace, p.off_rows);
   return a;
 }
 
 // Runs the dW pass: compacts the labelled rows (if that saves a 256-row
-// block), builds h^T of the rows swept, then the group pass.  Overwrites the
-// W^T area, so it comes after every pass that reads W^T.
+// block; their h rows overwrite the rows area, so it comes after every pass
+// that reads the dh pass's reordered rows), then the group pass.
 int dw_pass(BwdArgs& a, const Plan& p, void* workspace, hipStream_t s) {
-  if (launch_compact(a, at<int>(workspace, p.off_cnt), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
-  if (launch_transpose_dw_rows(a, at<uint16_t>(workspace, p.off_hT), s) != hipSuccess) return LMCE_ERR_HIP;
+  if (launch_compact(a, at<int>(workspace, p.off_cnt), p.L, s) != hipSuccess) return LMCE_ERR_HIP;
   return launch_group_pass(kPassDw, a, p, (p.V + 255) / 256, s);
 }
 
@@ -404,10 +396,9 @@ int bwd_common(int which, const void* h, const void* W, const int64_t* labels, c
   a.dW = dW_out;
   if (which & 1) {
     // the dh pass's own labelled-first order, in the compaction's row array
-    // (the dW pass rewrites it afterwards) and the h^T area (filled after)
+    // and the rows area (the dW pass rewrites both afterwards)
     if (launch_permute(a, at<int>(workspace, p.off_cnt), &hdr->dcompact, a.crow, nullptr, s) != hipSuccess)
       return LMCE_ERR_HIP;
-    if (launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
     st = launch_group_pass(kPassDh, a, p, (L + 255) / 256, s);
     if (st != LMCE_OK) return st;
   }
@@ -461,7 +452,6 @@ extern "C" int lmce_fwd_train(const void* h, const void* W, const int64_t* label
   a.O = dh_out;  // O rows live in the caller's dh buffer until lmce_bwd_train turns them into dh
   if (launch_permute(a, at<int>(workspace, p.off_cnt), &hdr->fcompact, a.fperm, a.finv, s) != hipSuccess)
     return LMCE_ERR_HIP;
-  if (launch_transpose(W, V, H, at<uint16_t>(workspace, p.off_WT), p.Vpad, s) != hipSuccess) return LMCE_ERR_HIP;
   st = launch_group_pass(kPassFwdDh, a, p, (L + 255) / 256, s);
   if (st != LMCE_OK) return st;
   // (max, sum) of every row came out as one log-sum-exp segment

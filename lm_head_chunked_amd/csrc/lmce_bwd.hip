@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void k_count_chunks(const int64_t* __restrict_
 
 // Decides the compaction (every block reaches the same decision from the
 // same counts) and writes, for the labelled rows of its chunk in order, their
-// index, label and lse.  ch_rows: rows the W^T area can hold.
+// index, label and lse.  ch_rows: rows the gathered-rows area can hold.
 __global__ __launch_bounds__(1024) void k_compact_rows(const int64_t* __restrict__ labels, const float* __restrict__ lse,
                                                        int64_t L, int64_t V, int64_t ignore_index, int64_t ch_rows,
                                                        const int* __restrict__ cnt, int nchunks, WsHeader* hdr,
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void k_gather_perm(const u16* __restrict__ h, 
   for (int64_t c = threadIdx.x; c < H / 8; c += 256) out[c] = in[c];
 }
 
-// h rows of the labelled rows, in order, into the W^T area (one row per
+// h rows of the labelled rows, in order, into the rows area (one row per
 // block; rows past the compaction's own count exit).
 __global__ __launch_bounds__(256) void k_gather_rows(const u16* __restrict__ h, int64_t H, const WsHeader* hdr,
                                                      const int* __restrict__ crow, u16* __restrict__ ch) {
@@ -202,34 +202,6 @@ __global__ __launch_bounds__(256) void k_gather_rows(const u16* __restrict__ h, 
   const uint4* in = reinterpret_cast<const uint4*>(h + src * H);
   uint4* out = reinterpret_cast<uint4*>(ch + (int64_t)blockIdx.x * H);
   for (int64_t c = threadIdx.x; c < H / 8; c += 256) out[c] = in[c];
-}
-
-// h^T (tile-major, as k_transpose) of the rows the dW pass sweeps: the
-// compacted rows when hdr->compact, else all L rows of h, zero up to the
-// next multiple of 128 rows.  The grid covers Lpad / 64 row tiles; tiles past
-// the swept rows' 128-row padding exit.
-__global__ __launch_bounds__(256) void k_transpose_dw_rows(const u16* __restrict__ h, const u16* __restrict__ ch,
-                                                           int64_t L, int64_t C, const WsHeader* hdr,
-                                                           u16* __restrict__ out) {
-  __shared__ u16 t[64][66];
-  const bool compact = hdr->compact != 0;
-  const u16* in = compact ? ch : h;
-  const int64_t R = compact ? (int64_t)hdr->n_compact : L;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  if (r0 >= (R + 127) / 128 * 128) return;
-  const int64_t c0 = (int64_t)blockIdx.y * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int rr = i >> 6, cc = i & 63;
-    const int64_t r = r0 + rr;
-    t[rr][cc] = (r < R) ? in[r * C + c0 + cc] : (u16)0;
-  }
-  __syncthreads();
-  const int64_t tile = r0 >> 7;
-  const int64_t rin = r0 & 127;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int cc = i >> 6, rr = i & 63;
-    out[(tile * C + c0 + cc) * 128 + rin + rr] = t[rr][cc];
-  }
 }
 
 // dW rows of the leftover blocks of the dW pass: block t of them was swept by
@@ -272,7 +244,8 @@ __device__ __forceinline__ int xcd_major(int b, int nwg) {
 // which is j % 8 for all groups when s is a multiple of 8.  The order of the
 // passes whose groups own row blocks when xcd_tiled does not apply: in a
 // round, member j of every group loads the same vocabulary tile of W (and the
-// same H slice of W^T), so groups that share an XCD read it through one L2.
+// same H columns of the round's W rows), so groups that share an XCD read it
+// through one L2.
 // The exchange then crosses XCDs, which its device-coherent stores and loads
 // allow.
 __device__ __forceinline__ int member_spread(int b) { return b; }
@@ -332,7 +305,7 @@ template <int HS>
 struct BwdCfg {
   static constexpr bool kPark = HS == 256;
   using P = TileGemm<256, 256, 4, 2, 0, 0, 0, kPark>;
-  using C = TileGemm<256, HS, 4, 2, kAuxSc1, 1, 1, true>;
+  using C = TileGemm<256, HS, 4, 2, kAuxSc1, 1, 2, true>;
   static constexpr int kLds = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
 };
 
@@ -402,8 +375,8 @@ __device__ __forceinline__ void gstage_flush(const char* lds, rsrc_t rslot, int 
 // B = h, so the tile is z^T: vocabulary on M, tokens on N), forms
 // G[token][v] and stores it as the member's two K-tiles of the round's slot
 // [256 tokens][K].  Then every member accumulates
-//   dh[rows][c0 .. c0+HS] += slot[256][K] * W^T[c0 .. c0+HS][round's vocabulary]
-// with K = 128 * (K-tiles in the round).
+//   dh[rows][c0 .. c0+HS] += slot[256][K] * W[round's vocabulary][c0 .. c0+HS]
+// with K = 128 * (K-tiles in the round), W's rows read MN-major (no copy).
 // Writes an accumulator tile of TileGemm's layout (rows row0 + ..., columns
 // col0 + ...) whose tile rows are positions pos0 + ... of a row order:
 // position pos goes to dh row perm[pos], columns c0 + ...; positions at or
@@ -528,11 +501,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
         return;
       const int ntl = min(2 * s, vt128 - k * 2 * s);
       const int64_t vbase = (int64_t)k * s * 256;
-      // A: the slot's K-tiles [256][128]; B: W^T tiles [H][128] of the round's
-      // vocabulary, rows c0 .. c0+HS (K-tiled)
+      // A: the slot's K-tiles [256][128]; B: the round's W rows (K = vocabulary),
+      // columns c0 .. c0+HS, read MN-major (rows past V read as zero)
+      const int64_t krows = min<int64_t>((int64_t)ntl * 128, V - vbase);
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
-             tiled_operand(p.WT + (vbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
-             lds, dacc);
+             linear_operand(p.W + vbase * H, (uint64_t)krows * H * 2, (uint32_t)(H * 2), (uint32_t)(c0 * 2)),
+             ntl * 128, lds, dacc);
       if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
     }
     // dh[r][c] for r < L (waves: wm token quarter, wn column half)
@@ -553,7 +527,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
 // of tokens [(k*s + j)*256, +256) against the group's vocabulary rows (A = h,
 // B = W: tokens on M, vocabulary on N), forms G^T[v][token] and stores it as
 // the member's two K-tiles of the round's slot [256 v][K].  Then
-//   dW[v rows][c0 .. c0+HS] += slot[256][K] * h^T[c0 .. c0+HS][round's tokens].
+//   dW[v rows][c0 .. c0+HS] += slot[256][K] * h[round's tokens][c0 .. c0+HS],
+// h's rows read MN-major (no copy).
 template <int HS>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   using P = typename BwdCfg<HS>::P;
@@ -673,9 +648,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
         return;
       const int ntl = min(2 * s, rt128 - k * 2 * s);
       const int64_t rbase = (int64_t)k * s * 256;
+      // B: the round's h rows (K = tokens), columns c0 .. c0+HS, read MN-major
+      // (rows past the swept ones read as zero)
+      const int64_t krows = min<int64_t>((int64_t)ntl * 128, L - rbase);
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
-             tiled_operand(p.hT + (rbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
-             lds, dacc);
+             linear_operand(hrows + rbase * H, (uint64_t)krows * H * 2, (uint32_t)(H * 2), (uint32_t)(c0 * 2)),
+             ntl * 128, lds, dacc);
       if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
     }
     // (an empty round range, e.g. no labelled rows at all, leaves 0)
@@ -896,9 +874,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (++nbar), p.spin_limit, p.hdr, &s_flag)) return;
       const int ntl = min(2 * s, vt128 - k * 2 * s);
       const int64_t vbase = (int64_t)k * s * 256;
+      const int64_t krows = min<int64_t>((int64_t)ntl * 128, V - vbase);
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
-             tiled_operand(p.WT + (vbase * H + c0 * 128), (uint64_t)ntl * H * 256, 256, (uint32_t)(H * 256)), ntl * 128,
-             lds, dacc);
+             linear_operand(p.W + vbase * H, (uint64_t)krows * H * 2, (uint32_t)(H * 2), (uint32_t)(c0 * 2)),
+             ntl * 128, lds, dacc);
       if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
     }
     // row sums: lane halves, the 4 waves, then the s members
@@ -1012,14 +991,6 @@ hipError_t launch_permute(const BwdArgs& a, int* cnt, int* flags, int* perm, int
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_dw_rows(const BwdArgs& a, void* hT, hipStream_t st) {
-  // every 64-row tile up to the 128-row padding: the rows past the swept ones
-  // must be written (as zeros), the dW pass's contraction reads them
-  dim3 grid((unsigned)(a.Lpad / 64), (unsigned)(a.H / 64));
-  hipLaunchKernelGGL(k_transpose_dw_rows, grid, dim3(256), 0, st, a.h, (const u16*)a.ch, a.L, a.H,
-                     (const WsHeader*)a.hdr, (u16*)hT);
-  return hipGetLastError();
-}
 
 hipError_t launch_dw_tail(const BwdArgs& a, int hs, hipStream_t st) {
   const int nvb = (int)((a.V + 255) / 256);

@@ -98,26 +98,12 @@ __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 
 
 // One wave-level LDS-DMA load moves 1 KiB: lane i lands at lds_base + 16*i,
 // i.e. rows r0 .. r0+7, physical slot i % 8, so the eight lanes of a row
-// read its whole 128-byte line.  The NW waves of the workgroup issue
-// ROWS/8/NW of them each.
-template <int ROWS, int NW, int AUX>
-__device__ __forceinline__ void stage_dma(rsrc_t rs, uint32_t ld_bytes, uint32_t col_bytes, char* region, int wave,
-                                          int lane) {
-  static_assert(ROWS % (8 * NW) == 0, "rows per stage must split evenly over the waves");
-#pragma unroll
-  for (int q = 0; q < ROWS / 8 / NW; ++q) {
-    const int r0 = (wave * (ROWS / 8 / NW) + q) * 8;
-    const int r = r0 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    const uint32_t voff = (uint32_t)r * ld_bytes + col_bytes + (uint32_t)c * 16u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LMCE_LDS_PTR(region + r0 * 128), 16, voff, 0, 0, AUX);
-  }
-}
+// read its whole 128-byte line (TileGemm::dma_one).
 
 // Fragment read from a stage through inline asm: the compiler's LDS-DMA
 // bookkeeping would otherwise put a full vmcnt(0) wait in front of every LDS
 // read and serialise the prefetch pipeline.  The caller waits for the reads
-// with lds_wait_frags() before using the fragments.
+// with lds_wait() before using the fragments.
 __device__ __forceinline__ bf16x8 stage_frag(const char* region, int row, int chunk) {
   const char* p = region + (row * 8 + (chunk ^ swz(row))) * 16;
   const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -126,42 +112,85 @@ __device__ __forceinline__ bf16x8 stage_frag(const char* region, int row, int ch
   return v;
 }
 
-// Waits until at most N LDS reads of this wave are outstanding (reads
-// complete in order, so the fragments issued before the last N are ready).
-// The fragments are tied to the wait so that no instruction using them is
-// scheduled before it.
-template <int N, int MB, int NB>
-__device__ __forceinline__ void lds_wait_frags_n(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
-  if constexpr (MB == 2 && NB == 4)
-    asm volatile("s_waitcnt lgkmcnt(%6)"
-                 : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]), "+v"(fb[3])
-                 : "n"(N));
-  else if constexpr (MB == 2 && NB == 2)
-    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]), "+v"(fb[1]) : "n"(N));
-  else
-    static_assert(MB == 0, "unsupported fragment count");
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ MN-major stages
+// An operand stored MN-major (element (k, r) at k * ld + col + 2 r: consecutive
+// rows r of one K index are contiguous) fills a stage as 64 K rows of R bf16
+// (2R bytes), 16-byte chunk c of K row kr in physical slot c ^ mn_swz(kr).
+// One LDS-DMA instruction moves 1 KiB, 1024 / 2R whole K rows, each lane one
+// chunk.  A fragment (the 32 x 16 K-major block the MFMA takes) is read with
+// two ds_read_b64_tr_b16: in a group of 16 lanes, lane k reads 4 consecutive
+// rows of one K row (8 bytes), and lane i of the group then holds 4
+// consecutive K values of one row.  With mn_swz, the 16 lanes of a read hit
+// distinct banks.
+__device__ __forceinline__ int mn_swz(int kr) { return (2 * (kr & 3)) ^ (8 * ((kr >> 3) & 1)); }
+
+template <int R, int AUX, class Op>
+__device__ __forceinline__ void mn_dma(const Op& o, int kt, int q, char* region, int lane) {
+  constexpr int kRowsPer = 1024 / (2 * R);  // K rows per instruction
+  const int kr = q * kRowsPer + lane / (R / 8);
+  const int c = (lane % (R / 8)) ^ mn_swz(kr);
+  const uint32_t voff = (uint32_t)(kt * 64 + kr) * o.ld + o.col + (uint32_t)c * 16u;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(o.rs, LMCE_LDS_PTR(region + q * 1024), 16, voff, 0, 0, AUX);
 }
 
-// Waits for every outstanding LDS read of this wave.  The fragments are
-// tied to the wait so that no instruction using them is scheduled before it.
-template <int MB, int NB>
-__device__ __forceinline__ void lds_wait_frags(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB]) {
-  static_assert(MB + NB <= 8, "at most 8 fragments per wait");
-  if constexpr (MB == 4 && NB == 4)
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]),
-                 "+v"(fb[2]), "+v"(fb[3]));
-  else if constexpr (MB == 4 && NB == 2)
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]));
-  else if constexpr (MB == 2 && NB == 4)
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]), "+v"(fb[1]), "+v"(fb[2]), "+v"(fb[3]));
-  else if constexpr (MB == 4 && NB == 1)
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]));
-  else if constexpr (MB == 2 && NB == 2)
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]), "+v"(fb[1]));
-  else if constexpr (MB == 2 && NB == 1)
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fb[0]));
-  else
-    static_assert(MB == 0, "unsupported fragment count");
+// MFMA operand fragments.  K-major stages (KT 0 and 1) give one ds_read_b128;
+// MN-major stages (KT 2) two transposing 8-byte reads.
+template <int KT>
+struct Frag {
+  static constexpr int kReads = 1;
+  bf16x8 v;
+};
+template <>
+struct Frag<2> {
+  static constexpr int kReads = 2;
+  u32x2 lo, hi;
+};
+
+__device__ __forceinline__ bf16x8 frag_value(const Frag<0>& f) { return f.v; }
+__device__ __forceinline__ bf16x8 frag_value(const Frag<1>& f) { return f.v; }
+__device__ __forceinline__ bf16x8 frag_value(const Frag<2>& f) {
+  const u32x4 v = {f.lo[0], f.lo[1], f.hi[0], f.hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// The fragment of rows rbase .. rbase + 31 (lane % 32) and K columns
+// 16 ks + 8 (lane / 32) .. + 7 of the stage part at `region` (R rows).
+template <int R, int KT>
+__device__ __forceinline__ void frag_read(Frag<KT>& f, const char* region, int rbase, int ks, int lane) {
+  if constexpr (KT == 2) {
+    const int g = lane >> 4, i = lane & 15;
+    const int kr = 16 * ks + 8 * (g >> 1) + (i >> 2);
+    const int r = rbase + 16 * (g & 1) + 4 * (i & 3);
+    const char* p0 = region + kr * (2 * R) + (((r >> 3) ^ mn_swz(kr)) << 4) + ((r & 7) << 1);
+    const char* p1 = region + (kr + 4) * (2 * R) + (((r >> 3) ^ mn_swz(kr + 4)) << 4) + ((r & 7) << 1);
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(f.lo) : "v"(lds_addr(p0)));
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(f.hi) : "v"(lds_addr(p1)));
+  } else {
+    f.v = stage_frag(region, rbase + (lane & 31), 2 * ks + (lane >> 5));
+  }
+}
+
+__device__ __forceinline__ void frag_tie(Frag<0>& f) { asm volatile("" : "+v"(f.v)); }
+__device__ __forceinline__ void frag_tie(Frag<1>& f) { asm volatile("" : "+v"(f.v)); }
+__device__ __forceinline__ void frag_tie(Frag<2>& f) { asm volatile("" : "+v"(f.lo), "+v"(f.hi)); }
+
+// s_waitcnt lgkmcnt(N), then every fragment register is tied to a point after
+// the wait (volatile asm statements keep their order), so that no use of a
+// fragment is scheduled before its read has landed.
+template <int N, class FA, int MB, class FB, int NB>
+__device__ __forceinline__ void lds_wait(FA (&fa)[MB], FB (&fb)[NB]) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+#pragma unroll
+  for (int i = 0; i < MB; ++i) frag_tie(fa[i]);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) frag_tie(fb[i]);
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -179,13 +208,16 @@ __device__ __forceinline__ void lds_wait_frags(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB
 // pair than issuing them in bursts after the barrier (run_staged).
 //
 // Operand addressing (bytes from the resource base): row r, K index k is at
-//   linear  (KT == 0):  r * ld + col + 2k
-//   K-tiled (KT == 1):  (k / 128) * tstride + r * ld + 2 (k % 128)
-// The K-tiled form reads matrices stored as consecutive [rows][128] blocks.
+//   linear   (KT == 0):  r * ld + col + 2k
+//   K-tiled  (KT == 1):  (k / 128) * tstride + r * ld + 2 (k % 128)
+//   MN-major (KT == 2):  k * ld + col + 2r  (r counted from the tile's first row)
+// The K-tiled form reads matrices stored as consecutive [rows][128] blocks; the
+// MN-major form reads a matrix whose rows are the K index (a row-major [K][M]
+// matrix used as the transposed operand) without any copy.
 struct Operand {
   rsrc_t rs;
-  uint32_t ld;       // bytes between rows
-  uint32_t col;      // linear: byte offset of the first K column
+  uint32_t ld;       // bytes between rows (MN-major: between K rows)
+  uint32_t col;      // linear: byte offset of the first K column; MN-major: of the first row
   uint32_t tstride;  // K-tiled: bytes between 128-wide K blocks
 };
 
@@ -208,18 +240,47 @@ struct TileGemm {
   static constexpr int STAGE_BYTES = (BM + BN) * 128;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static_assert(LDS_BYTES <= 144 * 1024, "leave LDS for the kernels' own arrays");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "rows per stage must split evenly over the waves");
+  static_assert((KTA != 2 || BM == 128 || BM == 256) && (KTB != 2 || BN == 128 || BN == 256),
+                "MN-major operands of 128 or 256 rows");
+  using FA = Frag<KTA>;
+  using FB = Frag<KTB>;
+
+  // DMA instruction q (of R / 8 / NW per wave) of one operand's part of a stage.
+  template <int R, int KT, int AUX>
+  __device__ __forceinline__ static void dma_one(const Operand& o, int kt, int q, char* region, int wave, int lane) {
+    if constexpr (KT == 2) {
+      mn_dma<R, AUX>(o, kt, wave * (R / 8 / NW) + q, region, lane);
+    } else {
+      const int r0 = (wave * (R / 8 / NW) + q) * 8;
+      const int r = r0 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      const uint32_t voff = (uint32_t)r * o.ld + k_offset<KT>(o, kt) + (uint32_t)c * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(o.rs, LMCE_LDS_PTR(region + r0 * 128), 16, voff, 0, 0, AUX);
+    }
+  }
 
   __device__ __forceinline__ static void issue(int kt, const Operand& a, const Operand& b, char* lds, int wave,
                                                int lane) {
     char* st = lds + (kt % STAGES) * STAGE_BYTES;
-    stage_dma<BM, NW, AUXA>(a.rs, a.ld, k_offset<KTA>(a, kt), st, wave, lane);
-    stage_dma<BN, NW, 0>(b.rs, b.ld, k_offset<KTB>(b, kt), st + BM * 128, wave, lane);
+#pragma unroll
+    for (int q = 0; q < BM / 8 / NW; ++q) dma_one<BM, KTA, AUXA>(a, kt, q, st, wave, lane);
+#pragma unroll
+    for (int q = 0; q < BN / 8 / NW; ++q) dma_one<BN, KTB, 0>(b, kt, q, st + BM * 128, wave, lane);
   }
 
   __device__ __forceinline__ static void run(const Operand& a, const Operand& b, int K, char* lds,
                                              f32x16 (&acc)[MB][NB]) {
     if constexpr (PF && STAGES == 2) run_interleaved(a, b, K, lds, acc);
     else run_staged(a, b, K, lds, acc);
+  }
+
+  // Fragments of sub-step ks (K columns 16 ks .. 16 ks + 15 of the stage at st).
+  __device__ __forceinline__ static void read_a(FA& f, const char* st, int mb, int ks, int wm, int lane) {
+    frag_read<BM>(f, st, wm * (BM / WM) + mb * 32, ks, lane);
+  }
+  __device__ __forceinline__ static void read_b(FB& f, const char* st, int nb, int ks, int wn, int lane) {
+    frag_read<BN>(f, st + BM * 128, wn * (BN / WN) + nb * 32, ks, lane);
   }
 
   __device__ __forceinline__ static void run_staged(const Operand& a, const Operand& b, int K, char* lds,
@@ -249,86 +310,68 @@ struct TileGemm {
       // the stage refilled here was last read in step kt - 1, whose reads
       // every wave completed before the barrier
       if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, a, b, lds, wave, lane);
-      const char* sa = lds + (kt % STAGES) * STAGE_BYTES;
-      const char* sb = sa + BM * 128;
+      const char* st = lds + (kt % STAGES) * STAGE_BYTES;
       if constexpr (PF) {
         // the next sub-step's fragments are read while this one's MFMAs run
-        bf16x8 fa[2][MB], fb[2][NB];
+        FA fa[2][MB];
+        FB fb[2][NB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) fa[0][mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), lane >> 5);
+        for (int mb = 0; mb < MB; ++mb) read_a(fa[0][mb], st, mb, 0, wm, lane);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fb[0][nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), lane >> 5);
+        for (int nb = 0; nb < NB; ++nb) read_b(fb[0][nb], st, nb, 0, wn, lane);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const int cur = ks & 1;
           if (ks + 1 < NKS) {
-            const int c = 2 * (ks + 1) + (lane >> 5);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              fa[cur ^ 1][mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), c);
+            for (int mb = 0; mb < MB; ++mb) read_a(fa[cur ^ 1][mb], st, mb, ks + 1, wm, lane);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              fb[cur ^ 1][nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), c);
-            lds_wait_frags_n<MB + NB>(fa[cur], fb[cur]);
+            for (int nb = 0; nb < NB; ++nb) read_b(fb[cur ^ 1][nb], st, nb, ks + 1, wn, lane);
+            lds_wait<MB * FA::kReads + NB * FB::kReads>(fa[cur], fb[cur]);
           } else {
-            lds_wait_frags_n<0>(fa[cur], fb[cur]);
+            lds_wait<0>(fa[cur], fb[cur]);
           }
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa[cur][mb], fb[cur][nb], acc[mb][nb]);
+            for (int nb = 0; nb < NB; ++nb)
+              acc[mb][nb] = mfma32(frag_value(fa[cur][mb]), frag_value(fb[cur][nb]), acc[mb][nb]);
         }
       } else {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const int c = 2 * ks + (lane >> 5);
-          bf16x8 fa[MB], fb[NB];
+          FA fa[MB];
+          FB fb[NB];
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) fa[mb] = stage_frag(sa, wm * (BM / WM) + mb * 32 + (lane & 31), c);
+          for (int mb = 0; mb < MB; ++mb) read_a(fa[mb], st, mb, ks, wm, lane);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) fb[nb] = stage_frag(sb, wn * (BN / WN) + nb * 32 + (lane & 31), c);
-          lds_wait_frags(fa, fb);
+          for (int nb = 0; nb < NB; ++nb) read_b(fb[nb], st, nb, ks, wn, lane);
+          lds_wait<0>(fa, fb);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(fa[mb], fb[nb], acc[mb][nb]);
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma32(frag_value(fa[mb]), frag_value(fb[nb]), acc[mb][nb]);
         }
       }
     }
   }
   // ---- interleaved schedule (two stages, fragment prefetch)
-  static constexpr int LA = BM / 8 / NW, LB = BN / 8 / NW;  // DMA instructions per wave: A rows, B rows
+  static constexpr int LA = BM / 8 / NW, LB = BN / 8 / NW;  // DMA instructions per wave: A part, B part
 
-  // One LDS-DMA instruction of stage kt: idx < LA moves 8 rows of A, else 8 rows of B (the same rows and
-  // slots as issue()).
+  // One LDS-DMA instruction of stage kt: idx < LA is one of the A part's, else one of the B part's (the
+  // same addresses and slots as issue()).
   __device__ __forceinline__ static void issue_one(int kt, int idx, const Operand& a, const Operand& b, char* lds,
                                                    int wave, int lane) {
     char* st = lds + (kt % STAGES) * STAGE_BYTES;
-    if (idx < LA) {
-      const int r0 = (wave * LA + idx) * 8;
-      const int r = r0 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
-      const uint32_t voff = (uint32_t)r * a.ld + k_offset<KTA>(a, kt) + (uint32_t)c * 16u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a.rs, LMCE_LDS_PTR(st + r0 * 128), 16, voff, 0, 0, AUXA);
-    } else {
-      const int r0 = (wave * LB + idx - LA) * 8;
-      const int r = r0 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
-      const uint32_t voff = (uint32_t)r * b.ld + k_offset<KTB>(b, kt) + (uint32_t)c * 16u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b.rs, LMCE_LDS_PTR(st + BM * 128 + r0 * 128), 16, voff, 0, 0, 0);
-    }
+    if (idx < LA) dma_one<BM, KTA, AUXA>(a, kt, idx, st, wave, lane);
+    else dma_one<BN, KTB, 0>(b, kt, idx - LA, st + BM * 128, wave, lane);
   }
 
   // Fragment j of sub-step ks of a stage: j < MB is A block j, else B block j - MB.
-  __device__ __forceinline__ static bf16x8 frag_j(const char* st, int j, int ks, int wm, int wn, int lane) {
-    const int c = 2 * ks + (lane >> 5);
-    if (j < MB) return stage_frag(st, wm * (BM / WM) + j * 32 + (lane & 31), c);
-    return stage_frag(st + BM * 128, wn * (BN / WN) + (j - MB) * 32 + (lane & 31), c);
-  }
-
-  __device__ __forceinline__ static void set_frag(bf16x8 (&fa)[MB], bf16x8 (&fb)[NB], int j, bf16x8 v) {
-    if (j < MB) fa[j] = v;
-    else fb[j - MB] = v;
+  __device__ __forceinline__ static void read_j(FA (&fa)[MB], FB (&fb)[NB], int j, const char* st, int ks, int wm,
+                                                int wn, int lane) {
+    if (j < MB) read_a(fa[j], st, j, ks, wm, lane);
+    else read_b(fb[j - MB], st, j - MB, ks, wn, lane);
   }
 
   // One K step over stage kt.  On entry the fragments of sub-step 0 are in
@@ -341,26 +384,27 @@ struct TileGemm {
   // which stage kt+1 is complete and stage kt's buffer can be refilled.
   template <bool NEXT, bool DMA>
   __device__ __forceinline__ static void step_interleaved(int kt, const Operand& a, const Operand& b, char* lds,
-                                                          int wave, int lane, int wm, int wn, bf16x8 (&fa)[2][MB],
-                                                          bf16x8 (&fb)[2][NB], f32x16 (&acc)[MB][NB]) {
+                                                          int wave, int lane, int wm, int wn, FA (&fa)[2][MB],
+                                                          FB (&fb)[2][NB], f32x16 (&acc)[MB][NB]) {
     const char* st = lds + (kt % STAGES) * STAGE_BYTES;
     const char* nx = lds + ((kt + 1) % STAGES) * STAGE_BYTES;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int cur = ks & 1;
-      lds_wait_frags_n<0>(fa[cur], fb[cur]);
+      lds_wait<0>(fa[cur], fb[cur]);
       if (NEXT && ks == NKS - 1) {
         wait_vmcnt<0>();
         raw_barrier();
       }
 #pragma unroll
       for (int i = 0; i < MB * NB; ++i) {
-        acc[i / NB][i % NB] = mfma32(fa[cur][i / NB], fb[cur][i % NB], acc[i / NB][i % NB]);
+        acc[i / NB][i % NB] =
+            mfma32(frag_value(fa[cur][i / NB]), frag_value(fb[cur][i % NB]), acc[i / NB][i % NB]);
         __builtin_amdgcn_sched_barrier(0);
         if (ks + 1 < NKS) {
-          if (i < MB + NB) set_frag(fa[cur ^ 1], fb[cur ^ 1], i, frag_j(st, i, ks + 1, wm, wn, lane));
+          if (i < MB + NB) read_j(fa[cur ^ 1], fb[cur ^ 1], i, st, ks + 1, wm, wn, lane);
         } else if (NEXT) {
-          if (i < MB + NB) set_frag(fa[cur ^ 1], fb[cur ^ 1], i, frag_j(nx, i, 0, wm, wn, lane));
+          if (i < MB + NB) read_j(fa[cur ^ 1], fb[cur ^ 1], i, nx, 0, wm, wn, lane);
           if (DMA && i < LA + LB) issue_one(kt + 2, i, a, b, lds, wave, lane);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -392,9 +436,10 @@ struct TileGemm {
       wait_vmcnt<0>();
     }
     raw_barrier();
-    bf16x8 fa[2][MB], fb[2][NB];
+    FA fa[2][MB];
+    FB fb[2][NB];
 #pragma unroll
-    for (int j = 0; j < MB + NB; ++j) set_frag(fa[0], fb[0], j, frag_j(lds, j, 0, wm, wn, lane));
+    for (int j = 0; j < MB + NB; ++j) read_j(fa[0], fb[0], j, lds, 0, wm, wn, lane);
     int kt = 0;
     for (; kt + 2 < nk; ++kt) step_interleaved<true, true>(kt, a, b, lds, wave, lane, wm, wn, fa, fb, acc);
     if (kt + 1 < nk) step_interleaved<true, false>(kt++, a, b, lds, wave, lane, wm, wn, fa, fb, acc);
@@ -439,8 +484,6 @@ __device__ __forceinline__ uint64_t pack_bf16x4(float a, float b, float c, float
   bf16x4 v = __builtin_convertvector((f32x4){a, b, c, d}, bf16x4);
   return __builtin_bit_cast(uint64_t, v);
 }
-
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // 8-byte buffer store, coherent at device scope (seen by sc1 loads of other
 // workgroups once the storing wave has waited for it).  voff is per lane,

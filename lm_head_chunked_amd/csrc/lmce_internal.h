@@ -65,9 +65,7 @@ struct BwdArgs {
   const int64_t* labels;
   const float* lse;
   const float* grad_loss;
-  const uint16_t* hT;   // h transposed tile-major: [Lpad/128][H][128], zero past L
-  const uint16_t* WT;   // W transposed tile-major: [Vpad/128][H][128], zero past V
-  int64_t L, H, V, ignore_index, Lpad, Vpad;
+  int64_t L, H, V, ignore_index;
   int group_size;       // workgroups per group = H / HS (HS = 256 if H % 256 == 0, else 128)
   int n_groups;
   int xcd_members;      // > 0: members of one group per XCD (xcd_tiled order); 0: the pass's default order
@@ -82,8 +80,8 @@ struct BwdArgs {
   float* part_s;        // [L] row sum of exp(z - max), fused forward output
   WsHeader* hdr;
   // The labelled rows in order (written by k_compact_rows when hdr->compact):
-  // their index, label and lse, and their h rows in the W^T area (free
-  // during the dW pass); the dW pass then sweeps hdr->n_valid rows.  Before
+  // their index, label and lse, and their h rows in the workspace's rows
+  // area; the dW pass then sweeps hdr->n_valid rows.  Before
   // that, crow holds the dh pass's labelled-first order when hdr->dcompact
   // (crow[position] = row, h rows in hp).
   int* crow;
@@ -93,7 +91,7 @@ struct BwdArgs {
   float* dw_part;       // [group][member][256][HS] partial dW slices of the dW pass's leftover blocks
   // Training forward on the rows reordered labelled-first (when hdr->fcompact):
   // fperm[position] = row, finv[row] = position, hp the reordered h rows (in
-  // the h^T area, free during the forward); blocks of unlabelled rows compute
+  // the rows area, free during the forward); blocks of unlabelled rows compute
   // lse only, and O, part_m, part_s are indexed by position.
   int* fperm;
   int* finv;
@@ -157,10 +155,9 @@ hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStre
 hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st, bool train = false,
                            const float* o_buf = nullptr);
 hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st);
-// Compaction of the labelled rows for the dW pass (cnt: ceil(L / 1024) ints),
-// then h^T of the rows the dW pass sweeps (compacted or all L).
+// Compaction of the labelled rows for the dW pass (cnt: ceil(L / 1024) ints)
+// and their h rows gathered into a.ch.
 hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream_t st);
-hipError_t launch_transpose_dw_rows(const BwdArgs& a, void* hT, hipStream_t st);
 // Labelled-first order of the rows, if it saves a 256-row block: flags[0] = 1
 // and flags[1] = labelled rows (else 0, 0), perm[position] = row, inv[row] =
 // position (inv may be null), and the reordered h rows in a.hp.  Used by the
