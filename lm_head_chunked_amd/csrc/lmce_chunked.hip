@@ -143,8 +143,8 @@ __global__ __launch_bounds__(1024) void k_chunk_loss(const float* __restrict__ n
 constexpr int64_t kMaxRows = int64_t(1) << 21;
 
 struct ChunkPlan {
-  int64_t L, H, V, cr, Vg, Rpad;
-  size_t off_Z, off_G, off_GT, off_hT, off_WT, off_part, off_nll, total;
+  int64_t L, H, V, cr, Vg;
+  size_t off_Z, off_G, off_part, off_nll, total;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -157,18 +157,17 @@ int chunk_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, ChunkPlan* p
   p->V = V;
   p->cr = chunk_rows < L ? chunk_rows : L;
   p->Vg = (V + 128 * kDhSplit - 1) / (128 * kDhSplit) * (128 * kDhSplit);
-  p->Rpad = (p->cr + 127) / 128 * 128;
+  // the operands read MN-major (W over one dh piece of the vocabulary, G over
+  // the chunk's rows) must fit one buffer resource, so that their 32-bit
+  // offsets stay exact
+  const int64_t kMaxRes = 0x7ffff000;
+  const int64_t rk = (p->cr + 63) / 64 * 64;
+  if ((p->Vg / kDhSplit + 1) * H * 2 > kMaxRes || rk * p->Vg * 2 > kMaxRes) return LMCE_ERR_UNSUPPORTED;
   size_t off = up256(sizeof(WsHeader));
   p->off_Z = off;
   off = up256(off + sizeof(float) * (size_t)p->cr * (size_t)p->Vg);
   p->off_G = off;
   off = up256(off + 2 * (size_t)p->cr * (size_t)p->Vg);
-  p->off_GT = off;
-  off = up256(off + 2 * (size_t)p->Rpad * (size_t)p->Vg);
-  p->off_hT = off;
-  off = up256(off + 2 * (size_t)p->Rpad * (size_t)H);
-  p->off_WT = off;
-  off = up256(off + 2 * (size_t)p->Vg * (size_t)H);
   p->off_part = off;
   off = up256(off + sizeof(float) * kDhSplit * (size_t)p->cr * (size_t)H);
   p->off_nll = off;
@@ -188,9 +187,11 @@ hipError_t chunk_logits(const ChunkPlan& p, const void* h, const void* W, int64_
   g.A = static_cast<const uint16_t*>(h) + r0 * p.H;
   g.a_bytes = (uint64_t)rows * p.H * 2;
   g.a_ld = (uint32_t)(p.H * 2);
+  g.a_form = 0;
   g.B = W;
   g.b_bytes = (uint64_t)p.V * p.H * 2;
   g.b_ld = (uint32_t)(p.H * 2);
+  g.b_form = 0;
   g.M = rows;
   g.N = p.V;
   g.kchunk = p.H;
@@ -256,31 +257,26 @@ extern "C" int lmce_chunked_bwd(const void* h, const void* W, const int64_t* lab
   hipStream_t s = static_cast<hipStream_t>(stream);
   WsHeader* hdr = reinterpret_cast<WsHeader*>(workspace);
   if (launch_count_labels(labels, L, V, ignore_index, hdr, -1, s) != hipSuccess) return LMCE_ERR_HIP;
-  uint16_t* WT = reinterpret_cast<uint16_t*>(at(workspace, p.off_WT));
-  // W^T, K-tiled over the vocabulary and zero up to Vg: the B operand of dh = G W
-  if (launch_transpose(W, V, H, WT, p.Vg, s) != hipSuccess) return LMCE_ERR_HIP;
   uint16_t* G = reinterpret_cast<uint16_t*>(at(workspace, p.off_G));
-  uint16_t* GT = reinterpret_cast<uint16_t*>(at(workspace, p.off_GT));
-  uint16_t* hT = reinterpret_cast<uint16_t*>(at(workspace, p.off_hT));
   float* part = reinterpret_cast<float*>(at(workspace, p.off_part));
   for (int64_t r0 = 0; r0 < L; r0 += p.cr) {
     const int64_t rows = (L - r0) < p.cr ? (L - r0) : p.cr;
-    const int64_t rpad = (rows + 127) / 128 * 128;
     if (chunk_logits(p, h, W, r0, rows, workspace, s) != hipSuccess) return LMCE_ERR_HIP;
     hipLaunchKernelGGL(k_chunk_grad, dim3((unsigned)rows), dim3(256), 0, s,
                        reinterpret_cast<const float*>(at(workspace, p.off_Z)), p.Vg, V, labels + r0, ignore_index,
                        grad_loss, (const WsHeader*)hdr, G, p.Vg);
     if (hipGetLastError() != hipSuccess) return LMCE_ERR_HIP;
-    // dh_c = G W: M = rows, N = H, K = Vg in kDhSplit pieces
+    // dh_c = G W: M = rows, N = H, K = Vg in kDhSplit pieces; W's rows are the
+    // K index, read MN-major (rows past V read as zero)
     GemmArgs d = {};
     d.A = G;
     d.a_bytes = (uint64_t)rows * p.Vg * 2;
     d.a_ld = (uint32_t)(p.Vg * 2);
-    d.B = WT;
-    d.b_bytes = (uint64_t)p.Vg * H * 2;
-    d.b_ld = 256;
-    d.b_tstride = (uint32_t)(H * 256);
-    d.b_tiled = 1;
+    d.a_form = 0;
+    d.B = W;
+    d.b_bytes = (uint64_t)V * H * 2;
+    d.b_ld = (uint32_t)(H * 2);
+    d.b_form = 2;
     d.M = rows;
     d.N = H;
     d.kchunk = p.Vg / kDhSplit;
@@ -295,24 +291,20 @@ extern "C" int lmce_chunked_bwd(const void* h, const void* W, const int64_t* lab
     hipLaunchKernelGGL(k_chunk_dh_sum, dim3((unsigned)rows), dim3(256), 0, s, (const float*)part, p.cr * H, H,
                        dh_out + r0 * H);
     if (hipGetLastError() != hipSuccess) return LMCE_ERR_HIP;
-    // dW += G^T h_c: M = V, N = H, K = the chunk's rows (K-tiled transposes, zero past rows)
-    if (launch_transpose(G, rows, p.Vg, GT, rpad, s) != hipSuccess) return LMCE_ERR_HIP;
-    if (launch_transpose(static_cast<const uint16_t*>(h) + r0 * H, rows, H, hT, rpad, s) != hipSuccess)
-      return LMCE_ERR_HIP;
+    // dW += G^T h_c: M = V, N = H, K = the chunk's rows; G and the chunk's h
+    // rows read MN-major (K rows past `rows` read as zero)
     GemmArgs w = {};
-    w.A = GT;
-    w.a_bytes = (uint64_t)rpad * p.Vg * 2;
-    w.a_ld = 256;
-    w.a_tstride = (uint32_t)(p.Vg * 256);
-    w.a_tiled = 1;
-    w.B = hT;
-    w.b_bytes = (uint64_t)rpad * H * 2;
-    w.b_ld = 256;
-    w.b_tstride = (uint32_t)(H * 256);
-    w.b_tiled = 1;
+    w.A = G;
+    w.a_bytes = (uint64_t)rows * p.Vg * 2;
+    w.a_ld = (uint32_t)(p.Vg * 2);
+    w.a_form = 2;
+    w.B = static_cast<const uint16_t*>(h) + r0 * H;
+    w.b_bytes = (uint64_t)rows * H * 2;
+    w.b_ld = (uint32_t)(H * 2);
+    w.b_form = 2;
     w.M = V;
     w.N = H;
-    w.kchunk = rpad;
+    w.kchunk = (rows + 63) / 64 * 64;
     w.ksplit = 1;
     w.epi = r0 == 0 ? kEpiStoreF32 : kEpiAccF32;
     w.alpha = 1.f;

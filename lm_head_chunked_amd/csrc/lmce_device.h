@@ -126,15 +126,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // distinct banks.
 __device__ __forceinline__ int mn_swz(int kr) { return (2 * (kr & 3)) ^ (8 * ((kr >> 3) & 1)); }
 
-template <int R, int AUX, class Op>
-__device__ __forceinline__ void mn_dma(const Op& o, int kt, int q, char* region, int lane) {
-  constexpr int kRowsPer = 1024 / (2 * R);  // K rows per instruction
-  const int kr = q * kRowsPer + lane / (R / 8);
-  const int c = (lane % (R / 8)) ^ mn_swz(kr);
-  const uint32_t voff = (uint32_t)(kt * 64 + kr) * o.ld + o.col + (uint32_t)c * 16u;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(o.rs, LMCE_LDS_PTR(region + q * 1024), 16, voff, 0, 0, AUX);
-}
-
 // MFMA operand fragments.  K-major stages (KT 0 and 1) give one ds_read_b128;
 // MN-major stages (KT 2) two transposing 8-byte reads.
 template <int KT>
@@ -250,7 +241,13 @@ struct TileGemm {
   template <int R, int KT, int AUX>
   __device__ __forceinline__ static void dma_one(const Operand& o, int kt, int q, char* region, int wave, int lane) {
     if constexpr (KT == 2) {
-      mn_dma<R, AUX>(o, kt, wave * (R / 8 / NW) + q, region, lane);
+      // MN-major: instruction qq moves K rows qq * 1024 / 2R .. of the stage, lane by lane in 16-byte chunks
+      constexpr int kRowsPer = 1024 / (2 * R);
+      const int qq = wave * (R / 8 / NW) + q;
+      const int kr = qq * kRowsPer + lane / (R / 8);
+      const int c = (lane % (R / 8)) ^ mn_swz(kr);
+      const uint32_t voff = (uint32_t)(kt * 64 + kr) * o.ld + o.col + (uint32_t)c * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(o.rs, LMCE_LDS_PTR(region + qq * 1024), 16, voff, 0, 0, AUX);
     } else {
       const int r0 = (wave * (R / 8 / NW) + q) * 8;
       const int r = r0 + (lane >> 3);

@@ -56,16 +56,15 @@ __device__ __forceinline__ bool gemm_tile(int b, const GemmArgs& p, int& tm, int
 }
 
 // Operand of the tile whose first row is r0, for the K piece starting at k0.
-template <int KT>
-__device__ __forceinline__ Operand gemm_operand(const void* base, uint64_t bytes, uint32_t ld, uint32_t tstride,
-                                                int64_t r0, int64_t k0) {
+template <int FORM>
+__device__ __forceinline__ Operand gemm_operand(const void* base, uint64_t bytes, uint32_t ld, int64_t r0, int64_t k0) {
   const char* b = static_cast<const char*>(base);
-  if constexpr (KT == 0) {
+  if constexpr (FORM == 0) {
     const uint64_t off = (uint64_t)r0 * ld;
     return linear_operand(b + off, bytes > off ? bytes - off : 0, ld, (uint32_t)(k0 * 2));
   } else {
-    const uint64_t off = (uint64_t)(k0 / 128) * tstride + (uint64_t)r0 * ld;
-    return tiled_operand(b + off, bytes > off ? bytes - off : 0, ld, tstride);
+    const uint64_t off = (uint64_t)k0 * ld;
+    return linear_operand(b + off, bytes > off ? bytes - off : 0, ld, (uint32_t)(r0 * 2));
   }
 }
 
@@ -117,16 +116,16 @@ __device__ __forceinline__ float frag_bf16(const u32x4 (&w)[2], int reg) {
 
 // Accumulator element (mb, nb, reg) of lane `lane` in wave (wm, wn) sits at
 // tile row wm*64 + mb*32 + acc_row(reg, lane), tile column wn*128 + nb*32 + lane%32.
-template <int KTA, int KTB>
+template <int FA, int FB>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
-  using G = TileGemm<256, 256, 4, 2, 0, KTA, KTB, true>;
+  using G = TileGemm<256, 256, 4, 2, 0, FA, FB, true>;
   __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
   int tm, tn;
   if (!gemm_tile(blockIdx.x, p, tm, tn)) return;  // uniform across the workgroup
   const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
   const int64_t k0 = (int64_t)blockIdx.y * p.kchunk;
-  const Operand oa = gemm_operand<KTA>(p.A, p.a_bytes, p.a_ld, p.a_tstride, m0, k0);
-  const Operand ob = gemm_operand<KTB>(p.B, p.b_bytes, p.b_ld, p.b_tstride, n0, k0);
+  const Operand oa = gemm_operand<FA>(p.A, p.a_bytes, p.a_ld, m0, k0);
+  const Operand ob = gemm_operand<FB>(p.B, p.b_bytes, p.b_ld, n0, k0);
   f32x16 acc[2][4];
   zero_acc(acc);
   G::run(oa, ob, (int)p.kchunk, lds, acc);
@@ -202,23 +201,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
     // 64 (i / 32) + i % 32 and + 32 of the gate/up GEMM, which stored them in fragment order:
     // this lane's are in that GEMM's tile (tm, 2 tn + wn), wave 2 wm + nb / 2, blocks
     // mb * 4 + 2 (nb % 2) (gate) and + 1 (up), at the same lane and registers.
-    // Outputs, staged through LDS one 32-unit column block nb at a time (64 units of the tile):
-    //  * d(gate/up) row-major at C, interleaved like the gate/up columns (the dx GEMM's A),
-    //  * K-tiled transposes [t_rows / 128][columns][128] of d(gate/up) at gT and of
-    //    silu(g) * u at aux (the weight-gradient GEMMs' operands over the chunk's rows).
-    // Rows from M up to t_rows come out as zeros (their acc and gate/up values are 0).
-    // LDS holds 192 columns (d(gate), d(up) of the two wave columns, then p) of 256 rows, in
-    // 8-byte units of four rows: unit (col, rq) at col * 64 + (rq ^ 2 (col % 16)), so that the
-    // lanes' 8-byte writes, the 16-byte column reads and the transposing reads below spread
-    // over the banks.
+    // Outputs, row-major: d(gate/up) at C, interleaved like the gate/up columns, and
+    // p = silu(g) * u at aux.  They pass through LDS one 32-unit column block nb at a time
+    // (64 units of the tile): 192 columns (d(gate), d(up) of the two wave columns, then p) of
+    // 256 rows in 8-byte units of four rows, unit (col, rq) at col * 64 + (rq ^ 2 (col % 16)),
+    // written by the lanes as they hold them and read back row-wise with transposing reads.
     const int64_t n2 = 2 * p.N;
     const int64_t ntg = (n2 + 255) / 256;  // tiles per tile row of the gate/up GEMM
-    const int tl = (int)min<int64_t>(256, p.t_rows - m0);  // rows of this tile in the K-tiled outputs
     const int64_t gtile = 2 * (int64_t)tn + wn;
     const rsrc_t rgu = make_rsrc(p.gu + ((int64_t)tm * ntg + gtile) * 65536, gtile < ntg ? 131072 : 0);
     const rsrc_t rdg = make_rsrc(static_cast<uint16_t*>(p.C) + m0 * n2, (uint64_t)rl * n2 * 2);
-    const rsrc_t rgT = make_rsrc(p.gT + (m0 / 128) * n2 * 128, (uint64_t)((tl + 127) / 128) * n2 * 128 * 2);
-    const rsrc_t raT = make_rsrc(p.aux + (m0 / 128) * p.N * 128, (uint64_t)((tl + 127) / 128) * p.N * 128 * 2);
+    const rsrc_t rpa = make_rsrc(p.aux + m0 * p.N, (uint64_t)rl * p.N * 2);
     uint64_t* st = reinterpret_cast<uint64_t*>(lds);
     auto unit = [](int col, int rq) { return col * 64 + (rq ^ (2 * (col & 15))); };
     // [mb][0..1] gate registers 0..7, 8..15; [mb][2..3] up
@@ -268,43 +261,31 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
       if (nb + 1 < 4) load_gu(nb + 1, gu[(nb + 1) & 1]);
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       raw_barrier();
-      // K-tiled transposes: 16 lanes move one column's 128-row block (256 contiguous bytes)
+      // Row-wise read-out with ds_read_b64_tr_b16.  In a group of 16 lanes, lane k reads rows
+      // 4 (rq0 + k % 4) .. + 3 of column c0 + k / 4; lane i then holds columns c0 .. c0 + 3 of
+      // row 4 rq0 + i.  Task t: rows 16 (t % 16) .., columns 32 (t / 16) ..; group g of the
+      // wave takes 8 of those columns (two reads), so each row gets 64 contiguous bytes.
+      // Column blocks 0 .. 3 are d(gate/up), 4 and 5 are p.
 #pragma unroll
       for (int s = 0; s < 12; ++s) {
-        const int w = s * kGemmThreads + (int)threadIdx.x;
-        const int col = w >> 5, blk = (w >> 4) & 1, ch = w & 15;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(st + unit(col, blk * 32 + 2 * ch));
-        const bool rows_in = blk * 128 < tl;
-        if (s < 8) {  // columns 0 .. 127: d(gate/up)
-          const int64_t gcol = 512 * (int64_t)tn + 256 * (col >> 6) + 64 * nb + (col & 63);
-          store_b128(rgT, (rows_in && gcol < n2) ? (uint32_t)(((blk * n2 + gcol) * 128 + ch * 8) * 2) : kDrop, v);
-        } else {      // columns 128 .. 191: p
-          const int a = col - 128;
-          const int64_t i = 256 * (int64_t)tn + 128 * (a >> 5) + 32 * nb + (a & 31);
-          store_b128(raT, (rows_in && i < p.N) ? (uint32_t)(((blk * p.N + i) * 128 + ch * 8) * 2) : kDrop, v);
-        }
-      }
-      // row-major d(gate/up): transposing reads (ds_read_b64_tr_b16).  In a group of 16 lanes,
-      // lane k reads rows 4 (rq0 + k % 4) .. + 3 of column c0 + k / 4; lane i then holds
-      // columns c0 .. c0 + 3 of row 4 rq0 + i.  Group g of the wave takes columns
-      // 32 cb + 8 g .. + 7 (two reads), so that each row gets 64 contiguous bytes.
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
         const int t = s * 8 + wave;
         const int rb = t & 15, cb = t >> 4;
         const int k = lane & 15, g = lane >> 4;
         const int c0 = 32 * cb + 8 * g + (k >> 2);
         const int rq = 4 * rb + (k & 3);
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(st + unit(c0, rq)));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(st + unit(c0 + 4, rq)));
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + unit(c0, rq)));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + unit(c0 + 4, rq)));
         const int r = 16 * rb + k;
-        const int cc = 32 * cb + 8 * g;
-        const int64_t gcol = 512 * (int64_t)tn + 256 * (cc >> 6) + 64 * nb + (cc & 63);
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 v = {l2[0], l2[1], h2[0], h2[1]};
-        store_b128(rdg, (r < rl && gcol < n2) ? (uint32_t)((r * n2 + gcol) * 2) : kDrop, v);
+        if (s < 8) {
+          const int cc = 32 * cb + 8 * g;
+          const int64_t gcol = 512 * (int64_t)tn + 256 * (cc >> 6) + 64 * nb + (cc & 63);
+          store_b128(rdg, (r < rl && gcol < n2) ? (uint32_t)((r * n2 + gcol) * 2) : kDrop, v);
+        } else {
+          const int64_t i = 256 * (int64_t)tn + 128 * (cb - 4) + 32 * nb + 8 * g;
+          store_b128(rpa, (r < rl && i < p.N) ? (uint32_t)((r * p.N + i) * 2) : kDrop, v);
+        }
       }
     }
   } else if (p.epi == kEpiAccF32Gu) {
@@ -343,10 +324,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   int64_t blocks = mt * nt;
   if (a.patch_m > 0) blocks = (blocks + 7) / 8 * 8;  // eight equal shares, one per XCD
   const dim3 grid((unsigned)blocks, (unsigned)a.ksplit);
-  if (a.a_tiled && a.b_tiled) hipLaunchKernelGGL((k_gemm<1, 1>), grid, dim3(kGemmThreads), 0, st, a);
-  else if (a.a_tiled) hipLaunchKernelGGL((k_gemm<1, 0>), grid, dim3(kGemmThreads), 0, st, a);
-  else if (a.b_tiled) hipLaunchKernelGGL((k_gemm<0, 1>), grid, dim3(kGemmThreads), 0, st, a);
-  else hipLaunchKernelGGL((k_gemm<0, 0>), grid, dim3(kGemmThreads), 0, st, a);
+  if (a.kchunk % 64 != 0) return hipErrorInvalidValue;
+  if (a.a_form == 0 && a.b_form == 0) hipLaunchKernelGGL((k_gemm<0, 0>), grid, dim3(kGemmThreads), 0, st, a);
+  else if (a.a_form == 0 && a.b_form == 2) hipLaunchKernelGGL((k_gemm<0, 2>), grid, dim3(kGemmThreads), 0, st, a);
+  else if (a.a_form == 2 && a.b_form == 2) hipLaunchKernelGGL((k_gemm<2, 2>), grid, dim3(kGemmThreads), 0, st, a);
+  else return hipErrorInvalidValue;  // no other pairing is instantiated
   return hipGetLastError();
 }
 

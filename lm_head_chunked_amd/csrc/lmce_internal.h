@@ -115,32 +115,31 @@ enum GemmEpi {
                       // tm * ceil(N / 256) + tn, 64 blocks (wave, mb, nb) of 64 lanes x 16 accumulator registers
   kEpiSwigluFwd = 3,  // acc = gate/up pairs (32-column blocks interleaved): C bf16 [M][ldc] = silu(g) * u at column i
   kEpiSwigluBwd = 4,  // acc = d(act) [M][N]: reads the gate/up values gu [M][2N] (interleaved) in fragment order;
-                      // C bf16 [M][2N] = d(gate/up) interleaved, and K-tiled transposes [t_rows / 128][cols][128]
-                      // of it (gT) and of silu(g) * u (aux), zero for rows M .. t_rows
+                      // C bf16 [M][2N] = d(gate/up) interleaved, aux bf16 [M][N] = silu(g) * u
   kEpiAccF32Gu = 5,   // C (gate rows) and C2 (up rows) fp32 [M/2][ldc] += alpha * acc, A rows interleaved
 };
 
 struct GemmArgs {
+  // Operand forms: 0 K-major (row r, K index k at r * ld + 2k), 2 MN-major
+  // (k * ld + 2r: a row-major [K][rows] matrix read transposed, in place).
   const void* A;
   uint64_t a_bytes;     // bytes readable from A
-  uint32_t a_ld, a_tstride;
-  int a_tiled;
+  uint32_t a_ld;
+  int a_form;
   const void* B;
   uint64_t b_bytes;
-  uint32_t b_ld, b_tstride;
-  int b_tiled;
+  uint32_t b_ld;
+  int b_form;
   int64_t M, N;
-  int64_t kchunk;       // K of one split piece
+  int64_t kchunk;       // K of one split piece (a multiple of 64)
   int ksplit;
   int epi;
   float alpha;
   void* C;
   void* C2;
   int64_t ldc, c_split;
-  const uint16_t* gu;   // kEpiSwigluBwd: gate/up values
-  uint16_t* gT;         // kEpiSwigluBwd: K-tiled d(gate/up)
-  uint16_t* aux;        // kEpiSwigluBwd: K-tiled silu(g) * u
-  int64_t t_rows;       // kEpiSwigluBwd: rows of the K-tiled outputs (a multiple of 128, >= M)
+  const uint16_t* gu;   // kEpiSwigluBwd: gate/up values (fragment order)
+  uint16_t* aux;        // kEpiSwigluBwd: silu(g) * u, row-major [M][N]
   int patch_m;          // tile order: patches of patch_m (1, 2, 4, 8) x (32 / patch_m) tiles, one patch per XCD
                         // at a time; 0: row-major
 };

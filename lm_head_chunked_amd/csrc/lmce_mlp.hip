@@ -13,17 +13,19 @@
 // Per call the library packs Wg and Wu into one [2I][H] matrix whose rows
 // alternate 32-row blocks of the two (rows 64q + j = Wg row 32q + j, rows
 // 64q + 32 + j = Wu row 32q + j), so that one GEMM gives each lane the gate
-// and up values of the same units, and writes K-tiled transposes of the
-// packed matrix and of Wd for the backward's contractions over I and H.
+// and up values of the same units.  Every other operand is read where it
+// lies: the GEMM engine reads a row-major matrix either K-major or, for the
+// contractions over the rows of another matrix, MN-major (transposing LDS
+// reads), so no transposed copy is made.
 //
 // Forward, per chunk c:  p_c = silu(x_c Wg^T) * (x_c Wu^T)   (GEMM, fused epilogue, bf16)
 //                        y_c = p_c Wd^T                      (GEMM, fp32 out)
 // Backward, per chunk c (upstream dy):
-//   gu_c = x_c [Wg; Wu]^T            recomputed (GEMM, bf16)
-//   dp_c = dy_c Wd, and in the same epilogue dg_c, du_c (bf16, row-major and K-tiled
-//          transposed) and p_c (bf16, K-tiled transposed)
-//   dx_c = dg_c Wg + du_c Wu          (one GEMM over the packed 2I)
-//   dWd += dy_c^T p_c, dWg += dg_c^T x_c, dWu += du_c^T x_c   (GEMMs, K = the chunk's rows)
+//   gu_c = x_c [Wg; Wu]^T            recomputed (GEMM, bf16, fragment order)
+//   dp_c = dy_c Wd (Wd read MN-major), and in the same epilogue dg_c, du_c and p_c (bf16, row-major)
+//   dx_c = dg_c Wg + du_c Wu          (one GEMM over the packed 2I, read MN-major)
+//   dWd += dy_c^T p_c, dWg += dg_c^T x_c, dWu += du_c^T x_c   (GEMMs over the chunk's rows, both
+//                                                               operands read MN-major)
 
 #include "lmce_device.h"
 #include "lmce_internal.h"
@@ -44,8 +46,8 @@ __global__ __launch_bounds__(256) void k_pack_gu(const uint16_t* __restrict__ Wg
 }
 
 struct MlpPlan {
-  int64_t L, H, I, cr, Rp;
-  size_t off_Wgu, off_WguT, off_WdT, off_gu, off_act, off_dgu, off_actT, off_dguT, off_dyT, off_xT, total;
+  int64_t L, H, I, cr;
+  size_t off_Wgu, off_gu, off_act, off_dgu, total;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -57,34 +59,22 @@ int mlp_plan(int64_t L, int64_t H, int64_t I, int64_t chunk_rows, MlpPlan* p) {
   p->H = H;
   p->I = I;
   p->cr = chunk_rows < L ? chunk_rows : L;
-  p->Rp = (p->cr + 127) / 128 * 128;
-  // every K-tiled operand (the packed weights over K = 2I, the chunk's
-  // gate/up gradient over K = its rows) must fit one buffer resource, so
-  // that its 32-bit offsets stay exact
+  // every operand read MN-major (the packed weights over K = 2I, Wd over
+  // K = H, the chunk's rows over K = its rows) must fit one buffer resource,
+  // so that its 32-bit offsets stay exact
   const int64_t kMaxRes = 0x7ffff000;
-  if (4 * I * H > kMaxRes || 4 * I * p->Rp > kMaxRes) return LMCE_ERR_UNSUPPORTED;
+  const int64_t rp = (p->cr + 63) / 64 * 64;
+  if (4 * I * H > kMaxRes || 4 * I * rp > kMaxRes) return LMCE_ERR_UNSUPPORTED;
   const size_t b = 2;  // bf16
   size_t off = up256(sizeof(WsHeader));
   p->off_Wgu = off;
   off = up256(off + b * 2 * I * H);
-  p->off_WguT = off;
-  off = up256(off + b * 2 * I * H);
-  p->off_WdT = off;
-  off = up256(off + b * H * I);
   p->off_gu = off;  // fragment order: whole 256 x 256 tiles
   off = up256(off + b * ((p->cr + 255) / 256 * 256) * ((2 * I + 255) / 256 * 256));
   p->off_act = off;
   off = up256(off + b * p->cr * I);
   p->off_dgu = off;
   off = up256(off + b * p->cr * 2 * I);
-  p->off_actT = off;
-  off = up256(off + b * p->Rp * I);
-  p->off_dguT = off;
-  off = up256(off + b * p->Rp * 2 * I);
-  p->off_dyT = off;
-  off = up256(off + b * p->Rp * H);
-  p->off_xT = off;
-  off = up256(off + b * p->Rp * H);
   p->total = off;
   return LMCE_OK;
 }
@@ -96,33 +86,32 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// A linear operand: `rows` rows of ld_elems bf16 each.
-void set_a_linear(GemmArgs& g, const void* p, int64_t rows, int64_t ld_elems) {
+// A K-major operand: `rows` rows of ld_elems bf16 each, K along a row.
+void set_a_kmajor(GemmArgs& g, const void* p, int64_t rows, int64_t ld_elems) {
   g.A = p;
   g.a_bytes = (uint64_t)rows * ld_elems * 2;
   g.a_ld = (uint32_t)(ld_elems * 2);
-  g.a_tiled = 0;
+  g.a_form = 0;
 }
-void set_b_linear(GemmArgs& g, const void* p, int64_t rows, int64_t ld_elems) {
+void set_b_kmajor(GemmArgs& g, const void* p, int64_t rows, int64_t ld_elems) {
   g.B = p;
   g.b_bytes = (uint64_t)rows * ld_elems * 2;
   g.b_ld = (uint32_t)(ld_elems * 2);
-  g.b_tiled = 0;
+  g.b_form = 0;
 }
-// A K-tiled operand as the transposer writes it: `rows` rows, K padded to kpad.
-void set_a_tiled(GemmArgs& g, const void* p, int64_t rows, int64_t kpad) {
+// An MN-major operand: a row-major matrix of k_rows rows (the K index) and
+// ld_elems columns (the operand's rows); K rows past k_rows read as zero.
+void set_a_mnmajor(GemmArgs& g, const void* p, int64_t k_rows, int64_t ld_elems) {
   g.A = p;
-  g.a_bytes = (uint64_t)rows * kpad * 2;
-  g.a_ld = 256;
-  g.a_tstride = (uint32_t)(rows * 256);
-  g.a_tiled = 1;
+  g.a_bytes = (uint64_t)k_rows * ld_elems * 2;
+  g.a_ld = (uint32_t)(ld_elems * 2);
+  g.a_form = 2;
 }
-void set_b_tiled(GemmArgs& g, const void* p, int64_t rows, int64_t kpad) {
+void set_b_mnmajor(GemmArgs& g, const void* p, int64_t k_rows, int64_t ld_elems) {
   g.B = p;
-  g.b_bytes = (uint64_t)rows * kpad * 2;
-  g.b_ld = 256;
-  g.b_tstride = (uint32_t)(rows * 256);
-  g.b_tiled = 1;
+  g.b_bytes = (uint64_t)k_rows * ld_elems * 2;
+  g.b_ld = (uint32_t)(ld_elems * 2);
+  g.b_form = 2;
 }
 
 // p_c = silu(g) * u of rows [r0, r0 + rows) into the act area; with
@@ -131,8 +120,8 @@ void set_b_tiled(GemmArgs& g, const void* p, int64_t rows, int64_t kpad) {
 hipError_t gate_up(const MlpPlan& p, const void* x, const uint16_t* Wgu, int64_t r0, int64_t rows, void* ws,
                    bool store_gu, hipStream_t s) {
   GemmArgs g = {};
-  set_a_linear(g, static_cast<const uint16_t*>(x) + r0 * p.H, rows, p.H);
-  set_b_linear(g, Wgu, 2 * p.I, p.H);
+  set_a_kmajor(g, static_cast<const uint16_t*>(x) + r0 * p.H, rows, p.H);
+  set_b_kmajor(g, Wgu, 2 * p.I, p.H);
   g.M = rows;
   g.N = 2 * p.I;
   g.kchunk = p.H;
@@ -150,17 +139,11 @@ hipError_t gate_up(const MlpPlan& p, const void* x, const uint16_t* Wgu, int64_t
   return launch_gemm(g, s);
 }
 
-// Packs Wg, Wu and writes the K-tiled transposes the backward reads.
-hipError_t prepare_weights(const MlpPlan& p, const void* Wg, const void* Wu, const void* Wd, void* ws, bool bwd,
-                           hipStream_t s) {
-  uint16_t* Wgu = at<uint16_t>(ws, p.off_Wgu);
+// Packs Wg and Wu into the interleaved [2I][H] matrix.
+hipError_t pack_weights(const MlpPlan& p, const void* Wg, const void* Wu, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(k_pack_gu, dim3((unsigned)(2 * p.I)), dim3(256), 0, s, static_cast<const uint16_t*>(Wg),
-                     static_cast<const uint16_t*>(Wu), p.H, Wgu);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !bwd) return e;
-  e = launch_transpose(Wgu, 2 * p.I, p.H, at<uint16_t>(ws, p.off_WguT), 2 * p.I, s);
-  if (e != hipSuccess) return e;
-  return launch_transpose(Wd, p.H, p.I, at<uint16_t>(ws, p.off_WdT), p.H, s);
+                     static_cast<const uint16_t*>(Wu), p.H, at<uint16_t>(ws, p.off_Wgu));
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -188,14 +171,14 @@ extern "C" int lmce_mlp_fwd(const void* x, const void* Wg, const void* Wu, const
     return LMCE_ERR_NULL;
   if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (prepare_weights(p, Wg, Wu, Wd, workspace, false, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (pack_weights(p, Wg, Wu, workspace, s) != hipSuccess) return LMCE_ERR_HIP;
   const uint16_t* Wgu = at<uint16_t>(workspace, p.off_Wgu);
   for (int64_t r0 = 0; r0 < L; r0 += p.cr) {
     const int64_t rows = (L - r0) < p.cr ? (L - r0) : p.cr;
     if (gate_up(p, x, Wgu, r0, rows, workspace, false, s) != hipSuccess) return LMCE_ERR_HIP;
     GemmArgs g = {};
-    set_a_linear(g, at<uint16_t>(workspace, p.off_act), rows, I);
-    set_b_linear(g, Wd, H, I);
+    set_a_kmajor(g, at<uint16_t>(workspace, p.off_act), rows, I);
+    set_b_kmajor(g, Wd, H, I);
     g.M = rows;
     g.N = H;
     g.kchunk = I;
@@ -222,7 +205,7 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     return LMCE_ERR_NULL;
   if (workspace_bytes < p.total) return LMCE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (prepare_weights(p, Wg, Wu, Wd, workspace, true, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (pack_weights(p, Wg, Wu, workspace, s) != hipSuccess) return LMCE_ERR_HIP;
   // the weight gradients are sums over the chunks: start from zero (a fill
   // kernel, which graph capture records as an ordinary node)
   if (launch_zero_u32(reinterpret_cast<unsigned*>(dWg_out), (int)(I * H), s) != hipSuccess ||
@@ -231,21 +214,18 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     return LMCE_ERR_HIP;
   const uint16_t* Wgu = at<uint16_t>(workspace, p.off_Wgu);
   uint16_t* gu = at<uint16_t>(workspace, p.off_gu);
+  uint16_t* act = at<uint16_t>(workspace, p.off_act);
   uint16_t* dgu = at<uint16_t>(workspace, p.off_dgu);
-  uint16_t* actT = at<uint16_t>(workspace, p.off_actT);
-  uint16_t* dguT = at<uint16_t>(workspace, p.off_dguT);
-  uint16_t* dyT = at<uint16_t>(workspace, p.off_dyT);
-  uint16_t* xT = at<uint16_t>(workspace, p.off_xT);
   const uint16_t* x16 = static_cast<const uint16_t*>(x);
   const uint16_t* dy16 = static_cast<const uint16_t*>(dy);
   for (int64_t r0 = 0; r0 < L; r0 += p.cr) {
     const int64_t rows = (L - r0) < p.cr ? (L - r0) : p.cr;
-    const int64_t rp = (rows + 127) / 128 * 128;
+    const int64_t rk = (rows + 63) / 64 * 64;  // K of the weight-gradient GEMMs (rows past `rows` read as zero)
     if (gate_up(p, x, Wgu, r0, rows, workspace, true, s) != hipSuccess) return LMCE_ERR_HIP;
-    // dp = dy_c Wd (B = Wd^T, K = H), epilogue: dg, du (packed like gu) and p
+    // dp = dy_c Wd (B = Wd read MN-major, K = H), epilogue: dg, du (packed like gu) and p
     GemmArgs d = {};
-    set_a_linear(d, dy16 + r0 * H, rows, H);
-    set_b_tiled(d, at<uint16_t>(workspace, p.off_WdT), I, H);
+    set_a_kmajor(d, dy16 + r0 * H, rows, H);
+    set_b_mnmajor(d, Wd, H, I);
     d.M = rows;
     d.N = I;
     d.kchunk = H;
@@ -254,15 +234,13 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     d.alpha = 1.f;
     d.C = dgu;
     d.gu = gu;
-    d.gT = dguT;
-    d.aux = actT;
-    d.t_rows = rp;
+    d.aux = act;
     d.patch_m = 4;
     if (launch_gemm(d, s) != hipSuccess) return LMCE_ERR_HIP;
-    // dx_c = [dg | du] [Wg; Wu] (B = the packed matrix transposed, K = 2I)
+    // dx_c = [dg | du] [Wg; Wu] (B = the packed matrix read MN-major, K = 2I)
     GemmArgs xg = {};
-    set_a_linear(xg, dgu, rows, 2 * I);
-    set_b_tiled(xg, at<uint16_t>(workspace, p.off_WguT), H, 2 * I);
+    set_a_kmajor(xg, dgu, rows, 2 * I);
+    set_b_mnmajor(xg, Wgu, 2 * I, H);
     xg.M = rows;
     xg.N = H;
     xg.kchunk = 2 * I;
@@ -273,17 +251,13 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     xg.ldc = H;
     xg.patch_m = 4;
     if (launch_gemm(xg, s) != hipSuccess) return LMCE_ERR_HIP;
-    // weight gradients: K = the chunk's rows, from K-tiled transposes (zero past `rows`):
-    // those of p and [dg | du] came out of the dp GEMM's epilogue
-    if (launch_transpose(dy16 + r0 * H, rows, H, dyT, rp, s) != hipSuccess ||
-        launch_transpose(x16 + r0 * H, rows, H, xT, rp, s) != hipSuccess)
-      return LMCE_ERR_HIP;
+    // weight gradients, K = the chunk's rows, both operands read MN-major
     GemmArgs wd = {};
-    set_a_tiled(wd, dyT, H, rp);
-    set_b_tiled(wd, actT, I, rp);
+    set_a_mnmajor(wd, dy16 + r0 * H, rows, H);
+    set_b_mnmajor(wd, act, rows, I);
     wd.M = H;
     wd.N = I;
-    wd.kchunk = rp;
+    wd.kchunk = rk;
     wd.ksplit = 1;
     wd.epi = kEpiAccF32;
     wd.alpha = 1.f;
@@ -292,11 +266,11 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     wd.patch_m = 4;
     if (launch_gemm(wd, s) != hipSuccess) return LMCE_ERR_HIP;
     GemmArgs wg = {};
-    set_a_tiled(wg, dguT, 2 * I, rp);
-    set_b_tiled(wg, xT, H, rp);
+    set_a_mnmajor(wg, dgu, rows, 2 * I);
+    set_b_mnmajor(wg, x16 + r0 * H, rows, H);
     wg.M = 2 * I;
     wg.N = H;
-    wg.kchunk = rp;
+    wg.kchunk = rk;
     wg.ksplit = 1;
     wg.epi = kEpiAccF32Gu;
     wg.alpha = 1.f;
