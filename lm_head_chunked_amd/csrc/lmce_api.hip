@@ -35,7 +35,7 @@ int spin_limit() {
 struct Plan {
   int64_t L, H, V;
   int chunk_rows, tile_rows, tiles_per_chunk, n_chunks, ntiles, segments, vtiles, vtiles_per_seg, xcd_map;
-  int hs, xbuf_wgs;
+  int hs, xbuf_wgs, gather_copy;
   size_t off_pm, off_ps, off_bsum, off_rows, off_sync, off_xbuf, off_park, off_xstat, off_cnt, off_crow,
       off_clab, off_clse, off_part, off_fperm, off_finv, total;
 };
@@ -81,10 +81,15 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   off = align256(off + sizeof(float) * (size_t)L * (size_t)p->segments);
   p->off_bsum = off;
   off = align256(off + sizeof(float) * (size_t)((L + 63) / 64));
-  // gathered h rows: the labelled-first rows of the training forward or of
-  // the dh pass, or the dW pass's compacted rows (one at a time)
+  // The group passes read h's rows in a labelled-first order or only the
+  // labelled ones through an index, with 32-bit buffer offsets from h.  Past
+  // 2^31 bytes of h they read a gathered copy instead (the labelled-first
+  // rows of the training forward or of the dh pass, or the dW pass's
+  // compacted rows, one at a time).
+  // Also with 128-wide slices (see k_bwd_dW's consumer).
+  p->gather_copy = ((uint64_t)L * (uint64_t)H * 2 > kMaxBufferBytes || p->hs == 128) ? 1 : 0;
   p->off_rows = off;
-  off = align256(off + sizeof(uint16_t) * (size_t)H * (size_t)L);
+  if (p->gather_copy) off = align256(off + sizeof(uint16_t) * (size_t)H * (size_t)L);
   p->off_sync = off;
   off = align256(off + sizeof(unsigned) * (size_t)kMaxBwdWGs * kSyncStride);
   p->off_xbuf = off;
@@ -318,7 +323,9 @@ int launch_group_pass(int pass, BwdArgs& a, const Plan& p, int64_t items, hipStr
   // 256-wide slices run both GEMMs on square tiles, but a group then holds
   // half as many workgroups: with fewer blocks than groups, half the chip
   // would idle, so such a pass takes 128-wide slices.
-  if (hs == 256 && items < resident / (p.H / 256)) {
+  // (Not the dW pass without a gathered copy: with 128-wide slices it reads
+  // the selected rows from that copy.)
+  if (hs == 256 && items < resident / (p.H / 256) && (pass != kPassDw || p.gather_copy)) {
     hs = 128;
     if (bwd_resident_wgs(pass, hs, &resident) != hipSuccess) return LMCE_ERR_HIP;
     if (resident > p.xbuf_wgs) resident = p.xbuf_wgs;
@@ -363,6 +370,7 @@ BwdArgs group_args(const Plan& p, const void* h, const void* W, const int64_t* l
   a.fperm = at<int>(workspace, p.off_fperm);
   a.finv = at<int>(workspace, p.off_finv);
   a.hp = at<uint16_t>(workspace, p.off_rows);
+  a.gather_copy = p.gather_copy;
   return a;
 }
 

@@ -304,9 +304,22 @@ constexpr int kBwdThreads = 512;
 template <int HS>
 struct BwdCfg {
   static constexpr bool kPark = HS == 256;
+  // producers: the logit tile; h's rows are the B operand (row-block passes) or the A operand (dW
+  // pass), read in place (P, PA) or through the row order or selection (gathered form: PG, PAG, a
+  // separate instantiation so that the in-order case keeps its registers)
   using P = TileGemm<256, 256, 4, 2, 0, 0, 0, kPark>;
+  using PG = TileGemm<256, 256, 4, 2, 0, 0, 3, kPark>;
+  using PA = TileGemm<256, 256, 4, 2, 0, 0, 0, kPark>;
+  using PAG = TileGemm<256, 256, 4, 2, 0, 3, 0, kPark>;
+  // consumers: the exchange slot against W's rows (row-block passes) or h's rows (dW pass), read MN-major;
+  // the dW pass's through the row selection (gathered form) with 256-wide slices only: the three-stage
+  // schedule of 128-wide slices would wait for its index loads, so with those the selected rows come
+  // from a gathered copy (the host plans one)
   using C = TileGemm<256, HS, 4, 2, kAuxSc1, 1, 2, true>;
+  using CH = TileGemm<256, HS, 4, 2, kAuxSc1, 1, HS == 256 ? 4 : 2, true>;
   static constexpr int kLds = P::LDS_BYTES > C::LDS_BYTES ? P::LDS_BYTES : C::LDS_BYTES;
+  static_assert(PG::LDS_BYTES == P::LDS_BYTES && PAG::LDS_BYTES == P::LDS_BYTES && CH::LDS_BYTES == C::LDS_BYTES,
+                "same stages");
 };
 
 // Parking area of one workgroup: accumulator register r of lane l of wave w
@@ -401,6 +414,7 @@ __device__ __forceinline__ void store_rows_perm(float* dh, const int* perm, int6
 template <int HS>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   using P = typename BwdCfg<HS>::P;
+  using PG = typename BwdCfg<HS>::PG;
   using C = typename BwdCfg<HS>::C;
   constexpr bool kPark = BwdCfg<HS>::kPark;
   __shared__ __attribute__((aligned(16))) char lds[BwdCfg<HS>::kLds];
@@ -428,7 +442,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   // order.  Each row's products and their order stay the same.
   const bool reordered = p.hdr->dcompact != 0;
   const int64_t n_lab = reordered ? (int64_t)p.hdr->d_n : L;
-  const u16* const hrows = reordered ? p.hp : p.h;
+  // h rows in the pass's order: through the order itself, or (when 32-bit
+  // offsets cannot reach all of h) from the gathered copy
+  const bool by_index = reordered && !p.gather_copy;
+  const u16* const hrows = reordered && p.gather_copy ? p.hp : p.h;
   unsigned epoch = 0;
 
   for (int rb = g; rb < nrb; rb += p.n_groups) {
@@ -452,7 +469,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
       scale[nb] = valid ? gscale : 0.f;
       lse2[nb] = t < rend ? p.lse[src] * kLog2e : INFINITY;  // rows past L: probability 0
     }
-    const Operand oh = linear_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
+    const Operand oh = by_index ? gathered_operand(p.h, (uint64_t)L * H * 2, (uint32_t)(H * 2), p.crow + r0,
+                                                   (int)(rend - r0))
+                                : gathered_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2),
+                                                   nullptr, (int)(rend - r0));
 
     f32x16 dacc[C::MB][C::NB];
     if constexpr (!kPark) zero_acc(dacc);
@@ -464,8 +484,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
         const int v0 = vt * 256;
         f32x16 z[P::MB][P::NB];
         zero_acc(z);
-        P::run(linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2)), oh, (int)H, lds,
-               z);
+        const Operand ow = linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
+        if (by_index) PG::run(ow, oh, (int)H, lds, z);
+        else P::run(ow, oh, (int)H, lds, z);
         // G[token][v] = scale * (exp(z - lse) - [v == y]), staged in LDS as
         // [token][v], 4 consecutive v per write.  Tile-local coordinates:
         // vl = v - v0, the label at lab - v0.
@@ -531,8 +552,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
 // h's rows read MN-major (no copy).
 template <int HS>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
-  using P = typename BwdCfg<HS>::P;
-  using C = typename BwdCfg<HS>::C;
+  using P = typename BwdCfg<HS>::PA;
+  using PAG = typename BwdCfg<HS>::PAG;
+  using C = typename BwdCfg<HS>::CH;
   constexpr bool kPark = BwdCfg<HS>::kPark;
   __shared__ __attribute__((aligned(16))) char lds[BwdCfg<HS>::kLds];
   __shared__ float row_lse2[256], row_scale[256];
@@ -552,7 +574,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   // the rows swept: the compacted labelled rows when hdr->compact, else all
   const bool compact = p.hdr->compact != 0;
   const int64_t L = compact ? (int64_t)p.hdr->n_compact : L_all;
-  const u16* const hrows = compact ? p.ch : p.h;
+  // h rows of the swept positions: through the selection itself, or (when
+  // 32-bit offsets cannot reach all of h) from the gathered copy
+  const bool by_index = compact && !p.gather_copy;  // (never with 128-wide slices: the host sees to that)
+  const u16* const hrows = compact && p.gather_copy ? p.ch : p.h;
   const int64_t* const labels = compact ? p.clab : p.labels;
   const float* const lse = compact ? p.clse : p.lse;
   const int rt256 = (int)((L + 255) / 256);
@@ -601,7 +626,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
         f32x16 z[P::MB][P::NB];
         zero_acc(z);
         // (the GEMM's first barrier orders the row_* writes before their use)
-        P::run(linear_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2)), ow, (int)H, lds, z);
+        const Operand oh = by_index ? gathered_operand(p.h, (uint64_t)L_all * H * 2, (uint32_t)(H * 2), p.crow + r0,
+                                                       (int)(rend - r0))
+                                    : gathered_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2,
+                                                       (uint32_t)(H * 2), nullptr, (int)(rend - r0));
+        if (by_index) PAG::run(oh, ow, (int)H, lds, z);
+        else P::run(oh, ow, (int)H, lds, z);
         // G^T[v][token]: lane = v (column), 4 consecutive tokens per store.
         // Token data is read once per 4-token group and reused for the
         // lane's 4 vocabulary columns; columns past V get a zero factor.
@@ -651,9 +681,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
       // B: the round's h rows (K = tokens), columns c0 .. c0+HS, read MN-major
       // (rows past the swept ones read as zero)
       const int64_t krows = min<int64_t>((int64_t)ntl * 128, L - rbase);
-      C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
-             linear_operand(hrows + rbase * H, (uint64_t)krows * H * 2, (uint32_t)(H * 2), (uint32_t)(c0 * 2)),
-             ntl * 128, lds, dacc);
+      const Operand ohk =
+          by_index ? gathered_operand(p.h, (uint64_t)L_all * H * 2, (uint32_t)(H * 2), p.crow + rbase, (int)krows,
+                                      (uint32_t)(c0 * 2))
+                   : gathered_operand(hrows + rbase * H, (uint64_t)krows * H * 2, (uint32_t)(H * 2), nullptr,
+                                      (int)krows, (uint32_t)(c0 * 2));
+      C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2), ohk, ntl * 128, lds, dacc);
       if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
     }
     // (an empty round range, e.g. no labelled rows at all, leaves 0)
@@ -739,6 +772,7 @@ __device__ __forceinline__ void gstage_flush_scaled(const char* lds, const float
 template <int HS>
 __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
   using P = typename BwdCfg<HS>::P;
+  using PG = typename BwdCfg<HS>::PG;
   using C = typename BwdCfg<HS>::C;
   constexpr bool kPark = BwdCfg<HS>::kPark;
   __shared__ __attribute__((aligned(16))) char lds[BwdCfg<HS>::kLds];
@@ -770,7 +804,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
   // a block (every output of this kernel is then indexed by position)
   const bool reordered = p.hdr->fcompact != 0;
   const int64_t n_lab = reordered ? (int64_t)p.hdr->f_n : L;
-  const u16* const hrows = reordered ? p.hp : p.h;
+  const bool by_index = reordered && !p.gather_copy;  // as in the dh pass
+  const u16* const hrows = reordered && p.gather_copy ? p.hp : p.h;
   unsigned epoch = 0, nbar = 0;
 
   for (int rb = g; rb < nrb; rb += p.n_groups) {
@@ -778,7 +813,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
     const int64_t rend = min(r0 + 256, L);
     // a block with no labelled row needs lse only: no P exchange, no O
     const bool o_block = r0 < n_lab;
-    const Operand oh = linear_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2));
+    const Operand oh = by_index ? gathered_operand(p.h, (uint64_t)L * H * 2, (uint32_t)(H * 2), p.fperm + r0,
+                                                   (int)(rend - r0))
+                                : gathered_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2),
+                                                   nullptr, (int)(rend - r0));
     if (t < 256) row_m[t] = -INFINITY;  // ordered by the barriers below
     float ssum[4] = {0.f, 0.f, 0.f, 0.f};  // lane's sums of exp(z - M) for its 4 tokens
     f32x16 dacc[C::MB][C::NB];
@@ -795,8 +833,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
         const int vlim = min((int)(V - v0), 256);
         f32x16 z[P::MB][P::NB];
         zero_acc(z);
-        P::run(linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2)), oh, (int)H, lds,
-               z);
+        const Operand ow = linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
+        if (by_index) PG::run(ow, oh, (int)H, lds, z);
+        else P::run(ow, oh, (int)H, lds, z);
         // per-token maximum of the tile: the lane's 32 values, the other lane
         // half, then the 4 waves that share the token
 #pragma unroll
@@ -972,6 +1011,7 @@ hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream
                      a.ignore_index, ch_rows, (const int*)cnt, nchunks, a.hdr, a.crow, a.clab, a.clse);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!a.gather_copy) return hipSuccess;  // the dW pass reads h through crow
   hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)a.L), dim3(256), 0, st, a.h, a.H, (const WsHeader*)a.hdr,
                      (const int*)a.crow, a.ch);
   return hipGetLastError();
@@ -986,6 +1026,7 @@ hipError_t launch_permute(const BwdArgs& a, int* cnt, int* flags, int* perm, int
                      (const int*)cnt, nchunks, flags, perm, inv);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!a.gather_copy) return hipSuccess;  // the pass reads h through perm
   hipLaunchKernelGGL(k_gather_perm, dim3((unsigned)a.L), dim3(256), 0, st, a.h, a.H, (const int*)flags,
                      (const int*)perm, a.hp);
   return hipGetLastError();

@@ -160,7 +160,7 @@ int chunk_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, ChunkPlan* p
   // the operands read MN-major (W over one dh piece of the vocabulary, G over
   // the chunk's rows) must fit one buffer resource, so that their 32-bit
   // offsets stay exact
-  const int64_t kMaxRes = 0x7ffff000;
+  const int64_t kMaxRes = (int64_t)kMaxBufferBytes;
   const int64_t rk = (p->cr + 63) / 64 * 64;
   if ((p->Vg / kDhSplit + 1) * H * 2 > kMaxRes || rk * p->Vg * 2 > kMaxRes) return LMCE_ERR_UNSUPPORTED;
   size_t off = up256(sizeof(WsHeader));

@@ -126,24 +126,30 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // distinct banks.
 __device__ __forceinline__ int mn_swz(int kr) { return (2 * (kr & 3)) ^ (8 * ((kr >> 3) & 1)); }
 
-// MFMA operand fragments.  K-major stages (KT 0 and 1) give one ds_read_b128;
-// MN-major stages (KT 2) two transposing 8-byte reads.
+// MFMA operand fragments.  K-major stages (forms 0, 1, 3) give one
+// ds_read_b128; MN-major stages (forms 2, 4) two transposing 8-byte reads.
 template <int KT>
 struct Frag {
   static constexpr int kReads = 1;
   bf16x8 v;
 };
-template <>
-struct Frag<2> {
+struct FragMN {
   static constexpr int kReads = 2;
   u32x2 lo, hi;
 };
+template <>
+struct Frag<2> : FragMN {};
+template <>
+struct Frag<4> : FragMN {};
 
-__device__ __forceinline__ bf16x8 frag_value(const Frag<0>& f) { return f.v; }
-__device__ __forceinline__ bf16x8 frag_value(const Frag<1>& f) { return f.v; }
-__device__ __forceinline__ bf16x8 frag_value(const Frag<2>& f) {
-  const u32x4 v = {f.lo[0], f.lo[1], f.hi[0], f.hi[1]};
-  return __builtin_bit_cast(bf16x8, v);
+template <int KT>
+__device__ __forceinline__ bf16x8 frag_value(const Frag<KT>& f) {
+  if constexpr (KT == 2 || KT == 4) {
+    const u32x4 v = {f.lo[0], f.lo[1], f.hi[0], f.hi[1]};
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    return f.v;
+  }
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
@@ -154,7 +160,7 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // 16 ks + 8 (lane / 32) .. + 7 of the stage part at `region` (R rows).
 template <int R, int KT>
 __device__ __forceinline__ void frag_read(Frag<KT>& f, const char* region, int rbase, int ks, int lane) {
-  if constexpr (KT == 2) {
+  if constexpr (KT == 2 || KT == 4) {
     const int g = lane >> 4, i = lane & 15;
     const int kr = 16 * ks + 8 * (g >> 1) + (i >> 2);
     const int r = rbase + 16 * (g & 1) + 4 * (i & 3);
@@ -167,9 +173,11 @@ __device__ __forceinline__ void frag_read(Frag<KT>& f, const char* region, int r
   }
 }
 
-__device__ __forceinline__ void frag_tie(Frag<0>& f) { asm volatile("" : "+v"(f.v)); }
-__device__ __forceinline__ void frag_tie(Frag<1>& f) { asm volatile("" : "+v"(f.v)); }
-__device__ __forceinline__ void frag_tie(Frag<2>& f) { asm volatile("" : "+v"(f.lo), "+v"(f.hi)); }
+template <int KT>
+__device__ __forceinline__ void frag_tie(Frag<KT>& f) {
+  if constexpr (KT == 2 || KT == 4) asm volatile("" : "+v"(f.lo), "+v"(f.hi));
+  else asm volatile("" : "+v"(f.v));
+}
 
 // s_waitcnt lgkmcnt(N), then every fragment register is tied to a point after
 // the wait (volatile asm statements keep their order), so that no use of a
@@ -202,14 +210,24 @@ __device__ __forceinline__ void lds_wait(FA (&fa)[MB], FB (&fb)[NB]) {
 //   linear   (KT == 0):  r * ld + col + 2k
 //   K-tiled  (KT == 1):  (k / 128) * tstride + r * ld + 2 (k % 128)
 //   MN-major (KT == 2):  k * ld + col + 2r  (r counted from the tile's first row)
+//   gathered linear   (KT == 3):  idx[r] * ld + col + 2k
+//   gathered MN-major (KT == 4):  idx[k] * ld + col + 2r
 // The K-tiled form reads matrices stored as consecutive [rows][128] blocks; the
 // MN-major form reads a matrix whose rows are the K index (a row-major [K][M]
-// matrix used as the transposed operand) without any copy.
+// matrix used as the transposed operand) without any copy.  The gathered forms
+// read the rows of a matrix through an index (a row order or a selection of
+// rows) instead of a gathered copy; their offsets idx * ld must stay below
+// 2^31 (the buffer range), and rows at or past nrows read as zero.
 struct Operand {
   rsrc_t rs;
   uint32_t ld;       // bytes between rows (MN-major: between K rows)
   uint32_t col;      // linear: byte offset of the first K column; MN-major: of the first row
   uint32_t tstride;  // K-tiled: bytes between 128-wide K blocks
+  const int* idx;    // gathered forms: row index of each operand row (form 3) or K row (form 4), null for
+                     // the identity
+  int nrows;         // gathered forms: rows (form 3) or K rows (form 4) that exist; the rest read as zero
+  uint32_t roff[4];  // form 3: byte offsets of this lane's DMA rows (the same in every K step)
+  int kidx;          // form 4: lane l holds idx of K row 8 wave + l % 8 of the K step whose DMA is issued next
 };
 
 template <int KT>
@@ -232,7 +250,8 @@ struct TileGemm {
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static_assert(LDS_BYTES <= 144 * 1024, "leave LDS for the kernels' own arrays");
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "rows per stage must split evenly over the waves");
-  static_assert((KTA != 2 || BM == 128 || BM == 256) && (KTB != 2 || BN == 128 || BN == 256),
+  static_assert(((KTA != 2 && KTA != 4) || BM == 128 || BM == 256) &&
+                    ((KTB != 2 && KTB != 4) || BN == 128 || BN == 256),
                 "MN-major operands of 128 or 256 rows");
   using FA = Frag<KTA>;
   using FB = Frag<KTB>;
@@ -240,20 +259,76 @@ struct TileGemm {
   // DMA instruction q (of R / 8 / NW per wave) of one operand's part of a stage.
   template <int R, int KT, int AUX>
   __device__ __forceinline__ static void dma_one(const Operand& o, int kt, int q, char* region, int wave, int lane) {
-    if constexpr (KT == 2) {
+    if constexpr (KT == 2 || KT == 4) {
       // MN-major: instruction qq moves K rows qq * 1024 / 2R .. of the stage, lane by lane in 16-byte chunks
       constexpr int kRowsPer = 1024 / (2 * R);
       const int qq = wave * (R / 8 / NW) + q;
       const int kr = qq * kRowsPer + lane / (R / 8);
       const int c = (lane % (R / 8)) ^ mn_swz(kr);
-      const uint32_t voff = (uint32_t)(kt * 64 + kr) * o.ld + o.col + (uint32_t)c * 16u;
+      uint32_t row;
+      if constexpr (KT == 2) {
+        row = (uint32_t)(kt * 64 + kr) * o.ld;
+      } else {
+        // this lane's K row among the wave's 8 of the step: q * kRowsPer + lane / (R / 8); its index is
+        // read from the lane of the wave that loaded it
+        const int sel = lane / (R / 8);
+        int cand[kRowsPer];  // read every candidate first, so that the selection stays branch-free
+#pragma unroll
+        for (int e = 0; e < kRowsPer; ++e) cand[e] = __builtin_amdgcn_readlane(o.kidx, q * kRowsPer + e);
+        int v = cand[0];
+#pragma unroll
+        for (int e = 1; e < kRowsPer; ++e) v = sel == e ? cand[e] : v;
+        const int krg = kt * 64 + wave * 8 + q * kRowsPer + sel;  // the K row, counted from the operand's first
+        if (o.idx == nullptr) v = krg;
+        row = krg < o.nrows ? (uint32_t)v * o.ld : kNoRow;
+      }
+      const uint32_t voff = row + o.col + (uint32_t)c * 16u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(o.rs, LMCE_LDS_PTR(region + qq * 1024), 16, voff, 0, 0, AUX);
+    } else if constexpr (KT == 3) {
+      const int r0 = (wave * (R / 8 / NW) + q) * 8;
+      const int r = r0 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      const uint32_t voff = o.roff[q] + o.col + (uint32_t)kt * 128u + (uint32_t)c * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(o.rs, LMCE_LDS_PTR(region + r0 * 128), 16, voff, 0, 0, AUX);
     } else {
       const int r0 = (wave * (R / 8 / NW) + q) * 8;
       const int r = r0 + (lane >> 3);
       const int c = (lane & 7) ^ swz(r);
       const uint32_t voff = (uint32_t)r * o.ld + k_offset<KT>(o, kt) + (uint32_t)c * 16u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(o.rs, LMCE_LDS_PTR(region + r0 * 128), 16, voff, 0, 0, AUX);
+    }
+  }
+
+  static constexpr uint32_t kNoRow = 0x80000000u;  // a row offset past every buffer range: reads zero
+
+
+
+  // Form 3: byte offsets of the rows this lane's DMA instructions move (the
+  // same rows in every K step), from the index with vector loads.
+  template <int R, int KT>
+  __device__ __forceinline__ static void gather_rows(Operand& o, int wave, int lane) {
+    if constexpr (KT == 3) {
+      static_assert(R / 8 / NW <= 4, "row offsets per lane");
+#pragma unroll
+      for (int q = 0; q < R / 8 / NW; ++q) {
+        const int r = (wave * (R / 8 / NW) + q) * 8 + (lane >> 3);
+        o.roff[q] = r < o.nrows ? (uint32_t)(o.idx ? o.idx[r] : r) * o.ld : kNoRow;
+      }
+    }
+  }
+  // Form 4: idx of the 8 consecutive K rows that the wave's DMA instructions
+  // move in K step kt, one per lane (lane l: K row 8 wave + l % 8), with a
+  // vector load whose range ends at nrows (past it: zero, unused).  Loaded
+  // ahead of the DMA; the DMA picks its rows with v_readlane after the
+  // stage's own vmcnt wait, so nothing waits for this load elsewhere.
+  template <int R, int KT>
+  __device__ __forceinline__ static void load_krows(Operand& o, int kt, int wave, int lane) {
+    if constexpr (KT == 4) {
+      static_assert((R / 8 / NW) * (1024 / (2 * R)) == 8 && R / 8 / NW <= 4, "8 K rows per wave and step");
+      if (o.idx != nullptr) {
+        const rsrc_t ri = make_rsrc(o.idx, (uint64_t)(o.nrows > 0 ? o.nrows : 0) * 4);
+        o.kidx = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)((kt * 64 + wave * 8 + (lane & 7)) * 4), 0, 0);
+      }
     }
   }
 
@@ -292,9 +367,21 @@ struct TileGemm {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     raw_barrier();
+    Operand aa = a, bb = b;  // gathered forms: this lane's row offsets
+    gather_rows<BM, KTA>(aa, wave, lane);
+    gather_rows<BN, KTB>(bb, wave, lane);
+    // gathered MN-major forms: each stage's K rows are loaded one DMA ahead,
+    // before the DMA issued in between, so the stage waits below cover them
+    Operand an = aa, bn = bb;  // the next stage's
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) issue(s, a, b, lds, wave, lane);
+      if (s < nk) {
+        load_krows<BM, KTA>(aa, s, wave, lane);
+        load_krows<BN, KTB>(bb, s, wave, lane);
+        issue(s, aa, bb, lds, wave, lane);
+      }
+    load_krows<BM, KTA>(an, STAGES - 1, wave, lane);
+    load_krows<BN, KTB>(bn, STAGES - 1, wave, lane);
     for (int kt = 0; kt < nk; ++kt) {
       // stage kt has landed (with three stages, kt + 1 may still be in flight)
       if constexpr (STAGES == 3) {
@@ -306,7 +393,13 @@ struct TileGemm {
       raw_barrier();
       // the stage refilled here was last read in step kt - 1, whose reads
       // every wave completed before the barrier
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, a, b, lds, wave, lane);
+      if (kt + STAGES - 1 < nk) {
+        aa = an;
+        bb = bn;
+        load_krows<BM, KTA>(an, kt + STAGES, wave, lane);  // for the next step's DMA, before this one
+        load_krows<BN, KTB>(bn, kt + STAGES, wave, lane);
+        issue(kt + STAGES - 1, aa, bb, lds, wave, lane);
+      }
       const char* st = lds + (kt % STAGES) * STAGE_BYTES;
       if constexpr (PF) {
         // the next sub-step's fragments are read while this one's MFMAs run
@@ -380,11 +473,15 @@ struct TileGemm {
   // for its own part of stage kt+1 and passes the workgroup barrier, after
   // which stage kt+1 is complete and stage kt's buffer can be refilled.
   template <bool NEXT, bool DMA>
-  __device__ __forceinline__ static void step_interleaved(int kt, const Operand& a, const Operand& b, char* lds,
-                                                          int wave, int lane, int wm, int wn, FA (&fa)[2][MB],
-                                                          FB (&fb)[2][NB], f32x16 (&acc)[MB][NB]) {
+  __device__ __forceinline__ static void step_interleaved(int kt, Operand& a, Operand& b, char* lds, int wave,
+                                                          int lane, int wm, int wn, FA (&fa)[2][MB], FB (&fb)[2][NB],
+                                                          f32x16 (&acc)[MB][NB]) {
     const char* st = lds + (kt % STAGES) * STAGE_BYTES;
     const char* nx = lds + ((kt + 1) % STAGES) * STAGE_BYTES;
+    if (DMA) {  // gathered MN-major forms: the K rows of stage kt + 2, read during this step
+      load_krows<BM, KTA>(a, kt + 2, wave, lane);
+      load_krows<BN, KTB>(b, kt + 2, wave, lane);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int cur = ks & 1;
@@ -425,9 +522,16 @@ struct TileGemm {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     raw_barrier();
     if (nk <= 0) return;
-    issue(0, a, b, lds, wave, lane);
+    Operand aa = a, bb = b;  // gathered forms: this lane's row offsets
+    gather_rows<BM, KTA>(aa, wave, lane);
+    gather_rows<BN, KTB>(bb, wave, lane);
+    load_krows<BM, KTA>(aa, 0, wave, lane);
+    load_krows<BN, KTB>(bb, 0, wave, lane);
+    issue(0, aa, bb, lds, wave, lane);
     if (nk > 1) {
-      issue(1, a, b, lds, wave, lane);
+      load_krows<BM, KTA>(aa, 1, wave, lane);
+      load_krows<BN, KTB>(bb, 1, wave, lane);
+      issue(1, aa, bb, lds, wave, lane);
       wait_vmcnt<LOADS>();
     } else {
       wait_vmcnt<0>();
@@ -438,9 +542,9 @@ struct TileGemm {
 #pragma unroll
     for (int j = 0; j < MB + NB; ++j) read_j(fa[0], fb[0], j, lds, 0, wm, wn, lane);
     int kt = 0;
-    for (; kt + 2 < nk; ++kt) step_interleaved<true, true>(kt, a, b, lds, wave, lane, wm, wn, fa, fb, acc);
-    if (kt + 1 < nk) step_interleaved<true, false>(kt++, a, b, lds, wave, lane, wm, wn, fa, fb, acc);
-    step_interleaved<false, false>(kt, a, b, lds, wave, lane, wm, wn, fa, fb, acc);
+    for (; kt + 2 < nk; ++kt) step_interleaved<true, true>(kt, aa, bb, lds, wave, lane, wm, wn, fa, fb, acc);
+    if (kt + 1 < nk) step_interleaved<true, false>(kt++, aa, bb, lds, wave, lane, wm, wn, fa, fb, acc);
+    step_interleaved<false, false>(kt, aa, bb, lds, wave, lane, wm, wn, fa, fb, acc);
   }
 };
 
@@ -450,6 +554,18 @@ __device__ __forceinline__ Operand linear_operand(const void* base, uint64_t byt
   o.ld = ld;
   o.col = col;
   o.tstride = 0;
+  o.idx = nullptr;
+  o.nrows = 0;
+  return o;
+}
+
+// Rows of `base` (ld bytes apart) through idx (null: rows 0, 1, ...); rows at
+// or past nrows read as zero.  For the gathered forms 3 and 4.
+__device__ __forceinline__ Operand gathered_operand(const void* base, uint64_t bytes, uint32_t ld, const int* idx,
+                                                    int nrows, uint32_t col = 0) {
+  Operand o = linear_operand(base, bytes, ld, col);
+  o.idx = idx;
+  o.nrows = nrows;
   return o;
 }
 
@@ -459,6 +575,8 @@ __device__ __forceinline__ Operand tiled_operand(const void* base, uint64_t byte
   o.ld = ld;
   o.col = 0;
   o.tstride = tstride;
+  o.idx = nullptr;
+  o.nrows = 0;
   return o;
 }
 

@@ -96,6 +96,11 @@ struct BwdArgs {
   int* fperm;
   int* finv;
   uint16_t* hp;
+  // 1: the reordered or compacted h rows are gathered into the rows area (hp,
+  // ch) and read from there; 0: they are read from h through the order or
+  // selection (when L * H * 2 bytes fit 32-bit buffer offsets) and hp, ch are
+  // unused
+  int gather_copy;
   float* dh;
   float* dW;
 };
@@ -118,6 +123,10 @@ enum GemmEpi {
                       // C bf16 [M][2N] = d(gate/up) interleaved, aux bf16 [M][N] = silu(g) * u
   kEpiAccF32Gu = 5,   // C (gate rows) and C2 (up rows) fp32 [M/2][ldc] += alpha * acc, A rows interleaved
 };
+
+// Largest byte range one buffer resource addresses exactly (make_rsrc clamps
+// to it); an operand whose offsets may go past it is read another way.
+constexpr uint64_t kMaxBufferBytes = 0x7ffff000ull;
 
 struct GemmArgs {
   // Operand forms: 0 K-major (row r, K index k at r * ld + 2k), 2 MN-major

@@ -62,7 +62,7 @@ int mlp_plan(int64_t L, int64_t H, int64_t I, int64_t chunk_rows, MlpPlan* p) {
   // every operand read MN-major (the packed weights over K = 2I, Wd over
   // K = H, the chunk's rows over K = its rows) must fit one buffer resource,
   // so that its 32-bit offsets stay exact
-  const int64_t kMaxRes = 0x7ffff000;
+  const int64_t kMaxRes = (int64_t)kMaxBufferBytes;
   const int64_t rp = (p->cr + 63) / 64 * 64;
   if (4 * I * H > kMaxRes || 4 * I * rp > kMaxRes) return LMCE_ERR_UNSUPPORTED;
   const size_t b = 2;  // bf16
