@@ -35,29 +35,6 @@
 
 namespace lmce {
 
-// Tile-major transpose: out holds, for each 128-row tile t of `in`, the
-// block [C][128] with out[(t*C + c)*128 + rr] = in[t*128 + rr][c] (0 past R).
-// A consumer slice (consecutive c) of one tile is then one contiguous block.
-// 64x64 tiles through LDS; C % 64 == 0, Rpad % 128 == 0.
-__global__ __launch_bounds__(256) void k_transpose(const u16* __restrict__ in, int64_t R, int64_t C,
-                                                   u16* __restrict__ out, int64_t Rpad) {
-  __shared__ u16 t[64][66];
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  const int64_t c0 = (int64_t)blockIdx.y * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int rr = i >> 6, cc = i & 63;
-    const int64_t r = r0 + rr;
-    t[rr][cc] = (r < R) ? in[r * C + c0 + cc] : (u16)0;
-  }
-  __syncthreads();
-  const int64_t tile = r0 >> 7;
-  const int64_t rin = r0 & 127;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int cc = i >> 6, rr = i & 63;
-    out[(tile * C + c0 + cc) * 128 + rin + rr] = t[rr][cc];
-  }
-}
-
 // ------------------------------------------------ labelled-row compaction
 // Rows without a label (ignore_index) carry no gradient: their G row is 0 and
 // they add nothing to dW.  When dropping them saves at least one 256-row
@@ -995,12 +972,6 @@ __global__ __launch_bounds__(256) void k_dh_finish(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------- launchers
-
-hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st) {
-  dim3 grid((unsigned)(Rpad / 64), (unsigned)(C / 64));
-  hipLaunchKernelGGL(k_transpose, grid, dim3(256), 0, st, (const u16*)in, R, C, (u16*)out, Rpad);
-  return hipGetLastError();
-}
 
 hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream_t st) {
   const int nchunks = (int)((a.L + 1023) / 1024);

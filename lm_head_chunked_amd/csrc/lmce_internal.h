@@ -162,7 +162,6 @@ hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStre
 // group waits all succeeded.
 hipError_t launch_fwd_rows(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st, bool train = false,
                            const float* o_buf = nullptr);
-hipError_t launch_transpose(const void* in, int64_t R, int64_t C, void* out, int64_t Rpad, hipStream_t st);
 // Compaction of the labelled rows for the dW pass (cnt: ceil(L / 1024) ints)
 // and their h rows gathered into a.ch.
 hipError_t launch_compact(const BwdArgs& a, int* cnt, int64_t ch_rows, hipStream_t st);
