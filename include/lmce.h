@@ -15,7 +15,7 @@
  * log-sum-exp.  The group-scheduled passes (the backward, and the training
  * forward) turn each tile into bf16 probabilities or G in registers and hand
  * it to the other workgroups of their group through a fixed exchange ring in
- * the workspace (at most 64 MiB), where it lives for the one round that
+ * the workspace (at most 128 MiB), where it lives for the one round that
  * consumes it: over a pass every logit crosses that ring once as 2 bytes,
  * L x V x 2 bytes in all, but never more than the ring at a time.
  *
@@ -77,7 +77,7 @@ const char* lmce_strerror(int status);
 /*
  * Bytes of device workspace that lmce_fwd / lmce_bwd and the training pair
  * need for this shape: per-row partials and orders (O(L) words), a fixed
- * exchange ring for the group passes (at most 64 MiB), for H >= 3072 a
+ * exchange ring for the group passes (at most 128 MiB), for H >= 3072 a
  * parking area for their accumulators (at most 64 MiB), and the dW pass's
  * partial slices (at most 64 MiB).  h and W are read in place, never copied
  * or transposed; the passes that skip unlabelled rows read h's rows through

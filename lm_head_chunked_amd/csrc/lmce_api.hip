@@ -99,7 +99,7 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   int64_t wgs = items * (H / 128);  // enough for either slice width
   if (wgs > kMaxBwdWGs) wgs = kMaxBwdWGs;
   p->xbuf_wgs = (int)wgs;
-  off = align256(off + (size_t)wgs * kXbufPerWG);
+  off = align256(off + (size_t)wgs * kXbufPerTile * round_tiles(p->hs));
   p->off_park = off;
   if (p->hs == 256) off = align256(off + (size_t)wgs * kParkPerWG);
   p->off_xstat = off;

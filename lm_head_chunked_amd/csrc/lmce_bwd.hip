@@ -8,12 +8,16 @@
 // not fit in one compute unit, so each pass runs as groups of s = H / HS
 // workgroups, workgroup j of a group owning an HS-wide slice of the
 // accumulator (HS = 128 in registers, or 256 parked in the workspace between
-// rounds).  In every round each member recomputes ONE full-H 256 x 256 logit
-// tile with MFMA, turns it into bf16 G in registers and writes it to the
-// group's exchange slot; after a group barrier every member contracts all s
-// tiles of the round into its own slice.  Each logit is thus recomputed
-// exactly once per pass and no logit or G tile exists for more than one
-// round (the exchange holds 2 x s tiles per group).
+// rounds).  In every round each member recomputes R = round_tiles(HS) full-H
+// 256 x 256 logit tiles with MFMA (two with 256-wide slices, one with
+// 128-wide), turns each into bf16 G (or P) in registers and writes it to the
+// group's exchange slot; after a group barrier every member contracts all
+// R x s tiles of the round into its own slice.  Each logit is thus
+// recomputed exactly once per pass and no logit or G tile exists for more
+// than one round (the exchange holds 2 x R x s tiles per group).  Two tiles
+// per round halve the group barriers and the parked accumulator's round
+// trips; four were slower (the exchange then outgrows what the last-level
+// cache keeps).
 //
 //   k_bwd_dh : group = 256 rows of h; rounds sweep the vocabulary, 256 per
 //              member; dh[rows][slice] += G W   (row-owned, no atomics)
@@ -360,11 +364,12 @@ __device__ __forceinline__ void gstage_flush(const char* lds, rsrc_t rslot, int 
 }
 
 // ---------------------------------------------------------------- dh pass
-// Group = 256 rows of h.  Round k: member j recomputes the logit tile of
-// vocabulary rows [(k*s + j)*256, +256) against the group's rows (A = W,
-// B = h, so the tile is z^T: vocabulary on M, tokens on N), forms
-// G[token][v] and stores it as the member's two K-tiles of the round's slot
-// [256 tokens][K].  Then every member accumulates
+// Group = 256 rows of h.  Round k: member j recomputes the logit tiles of
+// vocabulary rows [((k*R + e)*s + j)*256, +256), e < R = round_tiles(HS),
+// against the group's rows (A = W, B = h, so the tile is z^T: vocabulary on
+// M, tokens on N), forms G[token][v] and stores each as two K-tiles
+// (2(e*s + j), +1) of the round's slot [256 tokens][K].  Then every member
+// accumulates
 //   dh[rows][c0 .. c0+HS] += slot[256][K] * W[round's vocabulary][c0 .. c0+HS]
 // with K = 128 * (K-tiles in the round), W's rows read MN-major (no copy).
 // Writes an accumulator tile of TileGemm's layout (rows row0 + ..., columns
@@ -406,10 +411,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   const int64_t H = p.H, V = p.V, L = p.L;
   const int64_t c0 = (int64_t)j * HS;
   const rsrc_t park = make_rsrc(p.park + (int64_t)blockIdx.x * (kParkPerWG / 4), kPark ? kParkPerWG : 0);  // this workgroup's parking area
-  const int64_t slot_elems = (int64_t)s * 256 * 256;  // 2s K-tiles of [256][128]
+  constexpr int R = round_tiles(HS);
+  const int64_t slot_elems = (int64_t)R * s * 256 * 256;  // 2Rs K-tiles of [256][128]
   const int vt256 = (int)((V + 255) / 256);
   const int vt128 = (int)((V + 127) / 128);
-  const int rounds = (vt256 + s - 1) / s;
+  const int rounds = (vt256 + R * s - 1) / (R * s);
   const int nrb = (int)((L + 255) / 256);
   const int n_valid = p.hdr->n_valid;
   const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
@@ -456,40 +462,42 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
     for (int k = 0; k < rounds; ++k, ++epoch) {
       u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
       const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
-      const int vt = k * s + j;
-      if (vt < vt256) {
-        const int v0 = vt * 256;
-        f32x16 z[P::MB][P::NB];
-        zero_acc(z);
-        const Operand ow = linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
-        if (by_index) PG::run(ow, oh, (int)H, lds, z);
-        else P::run(ow, oh, (int)H, lds, z);
-        // G[token][v] = scale * (exp(z - lse) - [v == y]), staged in LDS as
-        // [token][v], 4 consecutive v per write.  Tile-local coordinates:
-        // vl = v - v0, the label at lab - v0.
-        const int vlim = min((int)(V - v0), 256);
-        raw_barrier();  // every wave is done with the GEMM's last LDS stage
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int yl = lab[nb] - v0;  // outside [0, 256) if the label is not in this tile
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              float gv[4];
-              const int vl0 = wm * 64 + mb * 32 + acc_row(qq * 4, lane);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float pr = exp2_fast(__builtin_fmaf(z[mb][nb][qq * 4 + e], kLog2e, -lse2[nb]));
-                pr = (vl0 + e == yl) ? pr - 1.f : pr;
-                gv[e] = pr * ((vl0 + e < vlim) ? scale[nb] : 0.f);
+      for (int e = 0; e < R; ++e) {
+        const int vt = (k * R + e) * s + j;
+        if (vt < vt256) {
+          const int v0 = vt * 256;
+          f32x16 z[P::MB][P::NB];
+          zero_acc(z);
+          const Operand ow = linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
+          if (by_index) PG::run(ow, oh, (int)H, lds, z);
+          else P::run(ow, oh, (int)H, lds, z);
+          // G[token][v] = scale * (exp(z - lse) - [v == y]), staged in LDS as
+          // [token][v], 4 consecutive v per write.  Tile-local coordinates:
+          // vl = v - v0, the label at lab - v0.
+          const int vlim = min((int)(V - v0), 256);
+          raw_barrier();  // every wave is done with the GEMM's last LDS stage
+  #pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int yl = lab[nb] - v0;  // outside [0, 256) if the label is not in this tile
+  #pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+              for (int qq = 0; qq < 4; ++qq) {
+                float gv[4];
+                const int vl0 = wm * 64 + mb * 32 + acc_row(qq * 4, lane);
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  float pr = exp2_fast(__builtin_fmaf(z[mb][nb][qq * 4 + e], kLog2e, -lse2[nb]));
+                  pr = (vl0 + e == yl) ? pr - 1.f : pr;
+                  gv[e] = pr * ((vl0 + e < vlim) ? scale[nb] : 0.f);
+                }
+                gstage_put(lds, wn * 128 + nb * 32 + (lane & 31), vl0, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
               }
-              gstage_put(lds, wn * 128 + nb * 32 + (lane & 31), vl0, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
-            }
-          __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          __syncthreads();
+          gstage_flush(lds, rslot, e * s + j);
         }
-        __syncthreads();
-        gstage_flush(lds, rslot, j);
       }
       if constexpr (kPark) {
         if (k == 0) zero_acc(dacc);
@@ -497,8 +505,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
       }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
         return;
-      const int ntl = min(2 * s, vt128 - k * 2 * s);
-      const int64_t vbase = (int64_t)k * s * 256;
+      const int ntl = min(2 * R * s, vt128 - k * 2 * R * s);
+      const int64_t vbase = (int64_t)k * R * s * 256;
       // A: the slot's K-tiles [256][128]; B: the round's W rows (K = vocabulary),
       // columns c0 .. c0+HS, read MN-major (rows past V read as zero)
       const int64_t krows = min<int64_t>((int64_t)ntl * 128, V - vbase);
@@ -521,10 +529,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------- dW pass
-// Group = 256 vocabulary rows.  Round k: member j recomputes the logit tile
-// of tokens [(k*s + j)*256, +256) against the group's vocabulary rows (A = h,
-// B = W: tokens on M, vocabulary on N), forms G^T[v][token] and stores it as
-// the member's two K-tiles of the round's slot [256 v][K].  Then
+// Group = 256 vocabulary rows.  Round k: member j recomputes the logit tiles
+// of tokens [((k*R + e)*s + j)*256, +256), e < R = round_tiles(HS), against the
+// group's vocabulary rows (A = h, B = W: tokens on M, vocabulary on N), forms
+// G^T[v][token] and stores each as two K-tiles (2(e*s + j), +1) of the
+// round's slot [256 v][K].  Then
 //   dW[v rows][c0 .. c0+HS] += slot[256][K] * h[round's tokens][c0 .. c0+HS],
 // h's rows read MN-major (no copy).
 template <int HS>
@@ -547,7 +556,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   const int64_t H = p.H, V = p.V, L_all = p.L;
   const int64_t c0 = (int64_t)j * HS;
   const rsrc_t park = make_rsrc(p.park + (int64_t)blockIdx.x * (kParkPerWG / 4), kPark ? kParkPerWG : 0);  // this workgroup's parking area
-  const int64_t slot_elems = (int64_t)s * 256 * 256;
+  constexpr int R = round_tiles(HS);
+  const int64_t slot_elems = (int64_t)R * s * 256 * 256;
   // the rows swept: the compacted labelled rows when hdr->compact, else all
   const bool compact = p.hdr->compact != 0;
   const int64_t L = compact ? (int64_t)p.hdr->n_compact : L_all;
@@ -559,7 +569,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   const float* const lse = compact ? p.clse : p.lse;
   const int rt256 = (int)((L + 255) / 256);
   const int rt128 = (int)((L + 127) / 128);
-  const int rounds = (rt256 + s - 1) / s;
+  const int rounds = (rt256 + R * s - 1) / (R * s);
   const int nvb = (int)((V + 255) / 256);
   const int n_valid = p.hdr->n_valid;
   const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
@@ -588,64 +598,66 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
     for (int k = k_begin; k < k_end; ++k, ++epoch) {
       u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
       const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
-      const int rt = k * s + j;
-      if (rt < rt256) {
-        const int64_t r0 = (int64_t)rt * 256;
-        const int64_t rend = min(r0 + 256, L);
-        if (threadIdx.x < 256) {
-          const int64_t t = r0 + threadIdx.x;
-          const int64_t y = t < rend ? labels[t] : p.ignore_index;
-          const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
-          row_lab[threadIdx.x] = (valid && y >= v0 && y < v0 + 256) ? (int)(y - v0) : -1;
-          row_scale[threadIdx.x] = valid ? gscale : 0.f;
-          row_lse2[threadIdx.x] = t < rend ? lse[t] * kLog2e : INFINITY;
-        }
-        f32x16 z[P::MB][P::NB];
-        zero_acc(z);
-        // (the GEMM's first barrier orders the row_* writes before their use)
-        const Operand oh = by_index ? gathered_operand(p.h, (uint64_t)L_all * H * 2, (uint32_t)(H * 2), p.crow + r0,
-                                                       (int)(rend - r0))
-                                    : gathered_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2,
-                                                       (uint32_t)(H * 2), nullptr, (int)(rend - r0));
-        if (by_index) PAG::run(oh, ow, (int)H, lds, z);
-        else P::run(oh, ow, (int)H, lds, z);
-        // G^T[v][token]: lane = v (column), 4 consecutive tokens per store.
-        // Token data is read once per 4-token group and reused for the
-        // lane's 4 vocabulary columns; columns past V get a zero factor.
-        const int vlim = (int)min<int64_t>(V - v0, 256);
-        raw_barrier();  // every wave is done with the GEMM's last LDS stage
-        float vmask[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) vmask[nb] = (wn * 128 + nb * 32 + (lane & 31) < vlim) ? 1.f : 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int tl0 = wm * 64 + mb * 32 + acc_row(qq * 4, lane);
-            float tlse[4], tsc[4];
-            int tlab[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              tlse[e] = row_lse2[tl0 + e];
-              tsc[e] = row_scale[tl0 + e];
-              tlab[e] = row_lab[tl0 + e];
-            }
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              const int vl = wn * 128 + nb * 32 + (lane & 31);
-              float gv[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float pr = exp2_fast(__builtin_fmaf(z[mb][nb][qq * 4 + e], kLog2e, -tlse[e]));
-                pr = (vl == tlab[e]) ? pr - 1.f : pr;
-                gv[e] = pr * (tsc[e] * vmask[nb]);
-              }
-              gstage_put(lds, vl, tl0, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
-            }
-            __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < R; ++e) {
+        const int rt = (k * R + e) * s + j;
+        if (rt < rt256) {
+          const int64_t r0 = (int64_t)rt * 256;
+          const int64_t rend = min(r0 + 256, L);
+          if (threadIdx.x < 256) {
+            const int64_t t = r0 + threadIdx.x;
+            const int64_t y = t < rend ? labels[t] : p.ignore_index;
+            const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
+            row_lab[threadIdx.x] = (valid && y >= v0 && y < v0 + 256) ? (int)(y - v0) : -1;
+            row_scale[threadIdx.x] = valid ? gscale : 0.f;
+            row_lse2[threadIdx.x] = t < rend ? lse[t] * kLog2e : INFINITY;
           }
-        __syncthreads();
-        gstage_flush(lds, rslot, j);
+          f32x16 z[P::MB][P::NB];
+          zero_acc(z);
+          // (the GEMM's first barrier orders the row_* writes before their use)
+          const Operand oh = by_index ? gathered_operand(p.h, (uint64_t)L_all * H * 2, (uint32_t)(H * 2), p.crow + r0,
+                                                         (int)(rend - r0))
+                                      : gathered_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2,
+                                                         (uint32_t)(H * 2), nullptr, (int)(rend - r0));
+          if (by_index) PAG::run(oh, ow, (int)H, lds, z);
+          else P::run(oh, ow, (int)H, lds, z);
+          // G^T[v][token]: lane = v (column), 4 consecutive tokens per store.
+          // Token data is read once per 4-token group and reused for the
+          // lane's 4 vocabulary columns; columns past V get a zero factor.
+          const int vlim = (int)min<int64_t>(V - v0, 256);
+          raw_barrier();  // every wave is done with the GEMM's last LDS stage
+          float vmask[4];
+  #pragma unroll
+          for (int nb = 0; nb < 4; ++nb) vmask[nb] = (wn * 128 + nb * 32 + (lane & 31) < vlim) ? 1.f : 0.f;
+  #pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int tl0 = wm * 64 + mb * 32 + acc_row(qq * 4, lane);
+              float tlse[4], tsc[4];
+              int tlab[4];
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                tlse[e] = row_lse2[tl0 + e];
+                tsc[e] = row_scale[tl0 + e];
+                tlab[e] = row_lab[tl0 + e];
+              }
+  #pragma unroll
+              for (int nb = 0; nb < 4; ++nb) {
+                const int vl = wn * 128 + nb * 32 + (lane & 31);
+                float gv[4];
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  float pr = exp2_fast(__builtin_fmaf(z[mb][nb][qq * 4 + e], kLog2e, -tlse[e]));
+                  pr = (vl == tlab[e]) ? pr - 1.f : pr;
+                  gv[e] = pr * (tsc[e] * vmask[nb]);
+                }
+                gstage_put(lds, vl, tl0, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          __syncthreads();
+          gstage_flush(lds, rslot, e * s + j);
+        }
       }
       if constexpr (kPark) {
         if (k == k_begin) zero_acc(dacc);
@@ -653,8 +665,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
       }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (epoch + 1), p.spin_limit, p.hdr, &s_flag))
         return;
-      const int ntl = min(2 * s, rt128 - k * 2 * s);
-      const int64_t rbase = (int64_t)k * s * 256;
+      const int ntl = min(2 * R * s, rt128 - k * 2 * R * s);
+      const int64_t rbase = (int64_t)k * R * s * 256;
       // B: the round's h rows (K = tokens), columns c0 .. c0+HS, read MN-major
       // (rows past the swept ones read as zero)
       const int64_t krows = min<int64_t>((int64_t)ntl * 128, L - rbase);
@@ -733,6 +745,35 @@ __device__ __forceinline__ void gstage_flush_scaled(const char* lds, const float
   }
 }
 
+// Slack of the training forward's reference: a tile's P is taken against the
+// running maximum while its own maximum exceeds that by at most this much
+// (P <= e^16, well inside bf16 and fp32 range), else against its own maximum.
+constexpr float kRefSlack = 16.f;
+
+// Multiplies the rows of the member's tile at slot position j (two K-tiles
+// written by gstage_flush from this same thread's chunks, long completed) by
+// fac[row], skipping the rows whose factor is exactly 1.
+__device__ __forceinline__ void gslot_rescale(rsrc_t rslot, const float* fac, int j) {
+  const int t = threadIdx.x;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int idx = i * 512 + t;
+    const int row = idx >> 5, c = idx & 31;
+    const float f = fac[row];
+    if (f != 1.f) {
+      const uint32_t voff = (uint32_t)(((c >> 4) * 256 * 128 + row * 128 + (c & 15) * 8) * 2) +
+                            (uint32_t)j * 2u * 256u * 128u * 2u;
+      const bf16x8 x = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rslot, voff, 0, kAuxSc1));
+      const f32x4 lo = {(float)x[0] * f, (float)x[1] * f, (float)x[2] * f, (float)x[3] * f};
+      const f32x4 hi = {(float)x[4] * f, (float)x[5] * f, (float)x[6] * f, (float)x[7] * f};
+      const bf16x4 blo = __builtin_convertvector(lo, bf16x4), bhi = __builtin_convertvector(hi, bf16x4);
+      const u32x4 w = {__builtin_bit_cast(u32x2, blo)[0], __builtin_bit_cast(u32x2, blo)[1],
+                       __builtin_bit_cast(u32x2, bhi)[0], __builtin_bit_cast(u32x2, bhi)[1]};
+      store_sc1_b128(rslot, voff, w);
+    }
+  }
+}
+
 // One vocabulary sweep per 256-row block yields both the log-sum-exp of every
 // row and O = sum_v softmax(z)_v W_v, so that dh = g/N * (O - W_y) needs no
 // second sweep (the gradient of the mean NLL, the definition on the pages
@@ -752,12 +793,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
   using PG = typename BwdCfg<HS>::PG;
   using C = typename BwdCfg<HS>::C;
   constexpr bool kPark = BwdCfg<HS>::kPark;
+  constexpr int R = round_tiles(HS);
   __shared__ __attribute__((aligned(16))) char lds[BwdCfg<HS>::kLds];
-  __shared__ float red[4][256];  // per-wave partial (max or sum) of each token
-  __shared__ float row_m[256];   // running maximum M of each token
-  __shared__ float row_l[256];   // this member's tile maximum m_j of each token
-  __shared__ float row_a[256];   // exp(M_old - M_new) (last: 1 / sum)
-  __shared__ float row_f[256];   // exp(m_j - M_new)
+  __shared__ float red[4][256];     // per-wave partial (max or sum) of each token
+  __shared__ float row_m[256];      // the group's running maximum M of each token (the reference)
+  __shared__ float row_a[256];      // exp(M_old - M_new) (last: 1 / sum)
+  __shared__ float row_s[256];      // sum of exp(z - M) over the tiles so far (this member's)
+  __shared__ float row_mx[256];     // this member's maximum over the round's tiles
+  __shared__ float row_r[R][256];   // reference r_u of tile u's P = exp(z - r_u)
+  __shared__ float row_ps[R][256];  // sum of tile u's P per token
+  __shared__ float row_f[R][256];   // exp(r_u - M_new): tile u's factor into the new reference
   __shared__ int s_flag;
 
   const int s = p.group_size;
@@ -770,12 +815,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
   const int64_t H = p.H, V = p.V, L = p.L;
   const int64_t c0 = (int64_t)j * HS;
   const rsrc_t park = make_rsrc(p.park + (int64_t)blockIdx.x * (kParkPerWG / 4), kPark ? kParkPerWG : 0);
-  const int64_t slot_elems = (int64_t)s * 256 * 256;
+  const int64_t slot_elems = (int64_t)R * s * 256 * 256;
   // this group's statistics exchange: [2][s][256] round maxima, [s][256] sums
   const rsrc_t rstat = make_rsrc(p.xstat + (int64_t)g * 3 * s * 256, (uint64_t)3 * s * 256 * 4);
   const int vt256 = (int)((V + 255) / 256);
   const int vt128 = (int)((V + 127) / 128);
-  const int rounds = (vt256 + s - 1) / s;
+  const int rounds = (vt256 + R * s - 1) / (R * s);
   const int nrb = (int)((L + 255) / 256);
   // rows in the labelled-first order when the host-side plan found it worth
   // a block (every output of this kernel is then indexed by position)
@@ -794,18 +839,35 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
                                                    (int)(rend - r0))
                                 : gathered_operand(hrows + r0 * H, (uint64_t)(rend - r0) * H * 2, (uint32_t)(H * 2),
                                                    nullptr, (int)(rend - r0));
-    if (t < 256) row_m[t] = -INFINITY;  // ordered by the barriers below
-    float ssum[4] = {0.f, 0.f, 0.f, 0.f};  // lane's sums of exp(z - M) for its 4 tokens
+    if (t < 256) {  // ordered by the barriers below
+      row_m[t] = -INFINITY;
+      row_s[t] = 0.f;
+    }
     f32x16 dacc[C::MB][C::NB];
     if constexpr (!kPark) zero_acc(dacc);
     for (int k = 0; k < rounds; ++k, ++epoch) {
       u16* slot = p.xbuf + ((int64_t)g * 2 + (epoch & 1)) * slot_elems;
       const rsrc_t rslot = make_rsrc(slot, (uint64_t)slot_elems * 2);
       const uint32_t xm = (uint32_t)((k & 1) * s * 256 * 4);  // this round's maxima slot (bytes)
-      const int vt = k * s + j;
-      const bool produce = vt < vt256;
-      float psum[4] = {0.f, 0.f, 0.f, 0.f};  // lane's sums of exp(z - m_j)
-      if (produce) {
+      if (t < 256) row_mx[t] = -INFINITY;
+      // The member's tiles u = 0 .. R-1 of the round.  Tile u's P is taken
+      // against r_u = the running reference M (the group's maximum before
+      // this round) when the tile's row maximum m_u stays within kRefSlack of
+      // it, else against m_u: P <= exp(kRefSlack) either way.  Every tile but
+      // the last goes to the slot at once (the next tile's GEMM needs the
+      // LDS); the last stays staged.  Once the group's new maximum M' is
+      // known each tile is brought to it with the factor exp(r_u - M'), which
+      // is exactly 1 for the rows whose reference did not move.
+#pragma unroll 1
+      for (int u = 0; u < R; ++u) {
+        const int vt = (k * R + u) * s + j;
+        if (vt >= vt256) {
+          if (t < 256) {
+            row_r[u][t] = -INFINITY;
+            row_ps[u][t] = 0.f;
+          }
+          continue;
+        }
         const int v0 = vt * 256;
         const int vlim = min((int)(V - v0), 256);
         f32x16 z[P::MB][P::NB];
@@ -830,12 +892,18 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
           if (lane < 32) red[wm][wn * 128 + nb * 32 + lane] = mx;
         }
         __syncthreads();  // also: every wave is done with the GEMM's LDS stages
-        if (t < 256) row_l[t] = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+        if (t < 256) {
+          const float m = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+          const float ref = row_m[t];
+          row_r[u][t] = m <= ref + kRefSlack ? ref : m;
+          row_mx[t] = fmaxf(row_mx[t], m);
+        }
         __syncthreads();
-        // P_j = exp(z - m_j), staged in LDS as [token][v]; columns past V are 0
+        // P_u = exp(z - r_u), staged in LDS as [token][v]; columns past V are 0
+        float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const float ml = row_l[wn * 128 + nb * 32 + (lane & 31)] * kLog2e;
+          const float ml = row_r[u][wn * 128 + nb * 32 + (lane & 31)] * kLog2e;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -852,26 +920,42 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
             }
           __builtin_amdgcn_sched_barrier(0);
         }
-      } else if (t < 256) {
-        row_l[t] = -INFINITY;
+        // the tile's sum per token: lane halves, then the 4 waves
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const float v = psum[nb] + __shfl_xor(psum[nb], 32);
+          if (lane < 32) red[wm][wn * 128 + nb * 32 + lane] = v;
+        }
+        __syncthreads();  // also: the staged tile is complete
+        if (t < 256) row_ps[u][t] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+        if (u < R - 1 && o_block) gstage_flush(lds, rslot, u * s + j);
       }
-      if (t < 256) store_sc1_b32(rstat, (uint32_t)t * 4u, xm + (uint32_t)j * 1024u, row_l[t]);
+      if (t < 256) store_sc1_b32(rstat, (uint32_t)t * 4u, xm + (uint32_t)j * 1024u, row_mx[t]);
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (++nbar), p.spin_limit, p.hdr, &s_flag)) return;
       if (t < 256) {
         const float old = row_m[t];
         const float mx = fmaxf(old, group_max(rstat, s, (uint32_t)t * 4u, xm));
-        row_a[t] = (old == -INFINITY) ? 0.f : exp2_fast((old - mx) * kLog2e);
-        row_f[t] = (row_l[t] == -INFINITY) ? 0.f : exp2_fast((row_l[t] - mx) * kLog2e);
+        const float a = (old == -INFINITY) ? 0.f : (old == mx ? 1.f : exp2_fast((old - mx) * kLog2e));
+        float sum = row_s[t] * a;
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+          const float r = row_r[u][t];
+          const float f = (r == -INFINITY) ? 0.f : (r == mx ? 1.f : exp2_fast((r - mx) * kLog2e));
+          row_f[u][t] = f;
+          sum = __builtin_fmaf(row_ps[u][t], f, sum);
+        }
+        row_a[t] = a;
+        row_s[t] = sum;
         row_m[t] = mx;
       }
       __syncthreads();
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int tok = wn * 128 + nb * 32 + (lane & 31);
-        ssum[nb] = __builtin_fmaf(ssum[nb], row_a[tok], psum[nb] * row_f[tok]);
-      }
       if (!o_block) continue;  // (uniform over the group: every member takes the same block)
-      if (produce) gstage_flush_scaled(lds, row_f, rslot, j);
+      // the last tile from LDS with its factor; the earlier ones in the slot,
+      // only the rows whose factor is not 1
+      if ((k * R + R - 1) * s + j < vt256) gstage_flush_scaled(lds, row_f[R - 1], rslot, (R - 1) * s + j);
+#pragma unroll 1
+      for (int u = 0; u < R - 1; ++u)
+        if ((k * R + u) * s + j < vt256) gslot_rescale(rslot, row_f[u], u * s + j);
       if constexpr (kPark) {
         if (k == 0) zero_acc(dacc);
         else unpark_acc(dacc, park, wave, lane);
@@ -888,24 +972,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_fwd_dh(BwdArgs p) {
           }
       }
       if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (++nbar), p.spin_limit, p.hdr, &s_flag)) return;
-      const int ntl = min(2 * s, vt128 - k * 2 * s);
-      const int64_t vbase = (int64_t)k * s * 256;
+      const int ntl = min(2 * R * s, vt128 - k * 2 * R * s);
+      const int64_t vbase = (int64_t)k * R * s * 256;
       const int64_t krows = min<int64_t>((int64_t)ntl * 128, V - vbase);
       C::run(tiled_operand(slot, (uint64_t)slot_elems * 2, 256, 256 * 128 * 2),
              linear_operand(p.W + vbase * H, (uint64_t)krows * H * 2, (uint32_t)(H * 2), (uint32_t)(c0 * 2)),
              ntl * 128, lds, dacc);
       if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
     }
-    // row sums: lane halves, the 4 waves, then the s members
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const float v = ssum[nb] + __shfl_xor(ssum[nb], 32);
-      if (lane < 32) red[wm][wn * 128 + nb * 32 + lane] = v;
-    }
-    __syncthreads();
-    if (t < 256)
-      store_sc1_b32(rstat, (uint32_t)t * 4u, (uint32_t)(2 * s * 1024 + j * 1024),
-                    (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]));
+    // row sums of the s members
+    if (t < 256) store_sc1_b32(rstat, (uint32_t)t * 4u, (uint32_t)(2 * s * 1024 + j * 1024), row_s[t]);
     if (!group_arrive_wait(p.sync + g * kSyncStride, (unsigned)s * (++nbar), p.spin_limit, p.hdr, &s_flag)) return;
     if (t < 256) {
       const float sum = group_sum(rstat, s, (uint32_t)t * 4u, (uint32_t)(2 * s * 1024));

@@ -16,7 +16,11 @@ constexpr int kStageK = 128;        // hidden-size granularity (the backward sli
 constexpr int kVTile = 256;         // vocabulary rows per forward logit tile
 constexpr int kSyncStride = 64;     // u32 words between two groups' counters (256 bytes)
 constexpr int kMaxBwdWGs = 256;     // upper bound of a backward cooperative grid
-constexpr int kXbufPerWG = 2 * 256 * 256 * 2;  // exchange bytes per backward workgroup (2 slots x one 256 x 256 bf16 tile)
+// Logit tiles each member of a group produces per round: two with 256-wide
+// H slices (half the group barriers and parked-accumulator round trips), one
+// with 128-wide slices (whose kernels have no registers to spare for it).
+constexpr int round_tiles(int hs) { return hs == 256 ? 2 : 1; }
+constexpr int kXbufPerTile = 2 * 256 * 256 * 2;  // exchange bytes per workgroup and tile of a round (2 slots)
 constexpr int kParkPerWG = 256 * 256 * 4;      // parked 256 x 256 fp32 accumulator slice per backward workgroup
 constexpr int kXstatPerWG = 3 * 256 * 4;       // fused forward: per-member round maxima (2 slots) and final sums
 
