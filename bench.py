@@ -92,6 +92,81 @@ def host_cores():
     return threads, nproc, model
 
 
+def _find_key(obj, key):
+    """The first value stored under `key` anywhere in a parsed JSON document."""
+    if isinstance(obj, dict):
+        if key in obj:
+            return obj[key]
+        obj = list(obj.values())
+    if isinstance(obj, list):
+        for v in obj:
+            if isinstance(v, (dict, list)):
+                try:
+                    return _find_key(v, key)
+                except KeyError:
+                    pass
+    raise KeyError(key)
+
+
+class UmcSampler:
+    """Samples the memory controllers' activity (amd-smi UMC_ACTIVITY, percent) of GPU 0 from a
+    background thread; mean() averages the samples taken inside [t0, t1]."""
+
+    def __init__(self):
+        import subprocess
+        import threading
+
+        self.samples, self.error = [], None
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    out = subprocess.run(["amd-smi", "metric", "-g", "0", "-u", "--json"], capture_output=True,
+                                         text=True, timeout=10).stdout
+                    u = _find_key(json.loads(out), "umc_activity")
+                    self.samples.append((time.time(), float(u["value"] if isinstance(u, dict) else u)))
+                except Exception as e:  # no amd-smi, or another output format: no estimate
+                    self.error = repr(e)
+                    time.sleep(0.5)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def mean(self, t0, t1):
+        v = [x for t, x in self.samples if t0 <= t <= t1]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+    def stop(self):
+        self._stop.set()
+
+
+def umc_copy_calibration(torch, sampler, seconds=3.0):
+    """UMC_ACTIVITY during back-to-back 2 GiB device copies, and the copies' byte rate (read +
+    written bytes per second by HIP events)."""
+    n = 1 << 31
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    e0.record()
+    k = 0
+    while time.time() - t0 < seconds:
+        for _ in range(8):
+            dst.copy_(src)
+        k += 8
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.time()
+    gbps = 2 * n * k / (e0.elapsed_time(e1) / 1e3) / 1e9
+    act, ns = sampler.mean(t0 + 0.5, t1)
+    del src, dst
+    return act, gbps, ns
+
+
 def cpu_baseline(wl, W_cpu, h_rows, y_rows, n_valid):
     """fp64 oracle on the first rows of the workload at full H and V, with
     its BLAS on every host core this process may use.
@@ -235,6 +310,10 @@ def main():
                          "(lmce_mlp_fwd + lmce_mlp_bwd) on --workload qwen3_4b_mlp_256k unless given")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (scale for HBM byte counters) and exit")
+    ap.add_argument("--dram-estimate", action="store_true",
+                    help="also estimate the DRAM traffic of the timed steps from the memory controllers' "
+                         "activity (amd-smi UMC_ACTIVITY), scaled by that of 2 GiB device copies of known rate; "
+                         "reported as dram_estimate (the sampling runs beside the timed steps)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -312,6 +391,12 @@ def main():
         if ev is not None:
             ev[len(calls)].record(stream)
 
+    sampler = None
+    if args.dram_estimate:
+        sampler = UmcSampler()
+        time.sleep(1.0)
+        cal_act, cal_gbps, cal_n = umc_copy_calibration(torch, sampler)
+        log(f"[bench] dram calibration: 2 GiB copies at {cal_gbps:.0f} GB/s, UMC_ACTIVITY {cal_act} % ({cal_n} samples)")
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
@@ -319,10 +404,12 @@ def main():
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    tu0 = time.time()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    tu1 = time.time()
     status = lm.lmce_read_status(ws)
     if status != _lib.LMCE_OK:
         raise RuntimeError(f"lmce status {status}: {_lib.strerror(status)}")
@@ -367,6 +454,20 @@ def main():
         "cpu_baseline": None,
         "parity": None,
     }
+    if sampler is not None:
+        sampler.stop()
+        act, ns = sampler.mean(tu0 + 0.3, tu1)
+        est = None
+        if act is not None and cal_act:
+            gbps = act / cal_act * cal_gbps
+            est = {"umc_activity_pct": act, "samples": ns, "copy_umc_activity_pct": cal_act,
+                   "copy_gbps": cal_gbps, "dram_gbps": gbps, "dram_bytes_per_step": gbps * 1e9 * ms_step / 1e3,
+                   "method": "amd-smi UMC_ACTIVITY over the timed steps, scaled by its value during 2 GiB device "
+                             "copies of measured byte rate (read + written)"}
+        result["dram_estimate"] = est if est is not None else {"error": sampler.error or "no samples"}
+        if est is not None:
+            log(f"[bench] dram estimate: UMC_ACTIVITY {act:.1f} % ({ns} samples) -> {est['dram_gbps']:.0f} GB/s, "
+                f"{est['dram_bytes_per_step'] / 1e9:.1f} GB per step")
     n_rows = min(args.cpu_rows, L)
     lse_rows = lse[:n_rows].cpu().numpy()
     dh_rows = dh[:n_rows].cpu().numpy()
