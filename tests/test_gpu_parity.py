@@ -150,18 +150,18 @@ def test_train_pair_parity(L, H, V, ign):
     assert np.all(gpu["dh"][ign_rows] == 0.0)
 
 
-def _max_jumps(z, s, jump=16.0):
+def _max_jumps(z, tiles, jump=16.0):
     """(jumps, flat) counts of vocabulary rounds after the first in which some
     row's running maximum rises by more than `jump` (or by no more), on fp64
-    logits z [L, V], with rows in 256-row blocks and rounds of s 256-column
-    tiles as in the fused training forward."""
+    logits z [L, V], with rows in 256-row blocks and rounds of `tiles`
+    256-column tiles as in the fused training forward."""
     L, V = z.shape
     jumps = flat = 0
     for r0 in range(0, L, 256):
         zb = z[r0:r0 + 256]
-        run = zb[:, :256 * s].max(axis=1)
-        for v0 in range(256 * s, V, 256 * s):
-            m = np.maximum(run, zb[:, v0:v0 + 256 * s].max(axis=1))
+        run = zb[:, :256 * tiles].max(axis=1)
+        for v0 in range(256 * tiles, V, 256 * tiles):
+            m = np.maximum(run, zb[:, v0:v0 + 256 * tiles].max(axis=1))
             if (m > run + jump).any():
                 jumps += 1
             else:
@@ -170,20 +170,28 @@ def _max_jumps(z, s, jump=16.0):
     return jumps, flat
 
 
-def test_train_pair_parity_when_the_maximum_jumps():
+# (L, H, V): 128-wide slices (3 members, one tile each per round) and
+# 256-wide slices (12 members, two tiles each per round)
+JUMPS = [(600, 384, 6000), (300, 3072, 30000)]
+
+
+@pytest.mark.parametrize("L,H,V", JUMPS)
+def test_train_pair_parity_when_the_maximum_jumps(L, H, V):
     """Logits that grow along the vocabulary, so that in later rounds of the
-    fused forward some rows' running maximum rises by more than 16 (O and the
-    row sums are then rescaled by less than exp(-16)), while in others it
-    barely moves."""
-    L, H, V = 600, 384, 6000
+    fused forward some rows' running maximum rises by more than 16 (O, the
+    row sums and, with two tiles per round, the tile already in the exchange
+    are then rescaled by less than exp(-16)), while in others it barely
+    moves."""
     say(f"[case] train pair, growing logits L={L} H={H} V={V}")
     h, W, y = synth.random_case(L, H, V, seed=23, w_std=0.05, ignore_frac=0.1)
     scale = torch.ones(V)
-    scale[3000:4500] = 8.0
-    scale[4500:] = 20.0
+    scale[V // 2:(3 * V) // 4] = 8.0
+    scale[(3 * V) // 4:] = 20.0
     W = (W.float() * scale[:, None]).to(torch.bfloat16)
     z = np32(h).astype(np.float64) @ np32(W).astype(np.float64).T
-    jumps, flat = _max_jumps(z, H // 128)
+    wide = H % 256 == 0 and H >= 3072
+    tiles = (H // 256) * 2 if wide else H // 128
+    jumps, flat = _max_jumps(z, tiles)
     assert jumps > 0 and flat > 0, (jumps, flat)
     a = run_gpu(h, W, y, grad=1.5, train=True)
     b = run_gpu(h, W, y, grad=1.5, train=True)
