@@ -310,7 +310,11 @@ struct BwdCfg {
 // no address register stays live across the transfers and they pipeline.
 template <int MB, int NB>
 __device__ __forceinline__ void park_acc(const f32x16 (&acc)[MB][NB], rsrc_t rs, int wave, int lane) {
-  const uint32_t voff = (uint32_t)lane * 4u;
+  // (a fresh value at every call: otherwise the compiler hoists the 16
+  // offsets voff + 256 e out of the round loop as registers of their own,
+  // instead of immediate offsets, and spills them)
+  uint32_t voff = (uint32_t)lane * 4u;
+  asm volatile("" : "+v"(voff));
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -322,7 +326,8 @@ __device__ __forceinline__ void park_acc(const f32x16 (&acc)[MB][NB], rsrc_t rs,
 
 template <int MB, int NB>
 __device__ __forceinline__ void unpark_acc(f32x16 (&acc)[MB][NB], rsrc_t rs, int wave, int lane) {
-  const uint32_t voff = (uint32_t)lane * 4u;
+  uint32_t voff = (uint32_t)lane * 4u;  // (fresh at every call, as in park_acc)
+  asm volatile("" : "+v"(voff));
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
