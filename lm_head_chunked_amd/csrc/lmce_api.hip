@@ -70,9 +70,12 @@ int make_plan(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, Plan* p) {
   p->segments = (p->vtiles + p->vtiles_per_seg - 1) / p->vtiles_per_seg;
   p->xcd_map = (p->segments == 8 && p->ntiles % 32 == 0) ? 1 : 0;
   // Widest H slice of one backward workgroup.  A 256-wide slice parks its
-  // accumulator (256 KiB out and back per round); the round's work grows with
-  // H, so the move pays off only for wide hidden sizes.
-  p->hs = (H % 256 == 0 && H >= 3072) ? 256 : 128;
+  // accumulator (256 KiB out and back per round of two logit tiles per
+  // member); the round's work grows with H, and from H = 1024 up the square
+  // tiles and the second tile per round win (Qwen3-4B head, H = 2560:
+  // training pair 507.5 against 454.0 ms; Qwen3-0.6B head, H = 1024: 11.25
+  // against 10.8 ms, same box).
+  p->hs = (H % 256 == 0 && H >= 1024) ? 256 : 128;
 
   size_t off = align256(sizeof(WsHeader));
   p->off_pm = off;

@@ -83,7 +83,7 @@ def test_workspace_never_holds_the_logits():
         # bytes); no transposed copy of h or W (the GEMMs read both in
         # place), never L * V, and no L x H fp32 array (the training
         # forward's O lives in the caller's dh)
-        gathered = wl.H < 3072 or wl.H % 256 != 0 or wl.L * wl.H * 2 > 0x7ffff000
+        gathered = wl.H < 1024 or wl.H % 256 != 0 or wl.L * wl.H * 2 > 0x7ffff000
         bound = (2 * wl.L * wl.H if gathered else 0) + 96 * wl.L + (264 << 20)
         assert ws <= bound, (wl.name, ws, bound)
         if not gathered:

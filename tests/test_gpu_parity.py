@@ -101,13 +101,15 @@ def test_ragged_shapes(L, H, V, ign):
     assert_parity(gpu, ref, f"L={L} H={H} V={V}")
 
 
-# Wide hidden sizes (H % 256 == 0, H >= 3072) give each backward workgroup a
+# Wide hidden sizes (H % 256 == 0, H >= 1024) give each backward workgroup a
 # 256-wide slice whose accumulator is parked between rounds, when the pass has
 # at least one row block (dh) or vocabulary block (dW) per group: many rows
 # exercise the dh pass that way, a large vocabulary the dW pass.
 WIDE = [
     (5500, 3072, 2500, 0.1),
     (600, 3072, 5500, 0.1),
+    (7000, 1024, 3000, 0.2),
+    (900, 2560, 9000, 0.1),
 ]
 
 
@@ -189,7 +191,7 @@ def test_train_pair_parity_when_the_maximum_jumps(L, H, V):
     scale[(3 * V) // 4:] = 20.0
     W = (W.float() * scale[:, None]).to(torch.bfloat16)
     z = np32(h).astype(np.float64) @ np32(W).astype(np.float64).T
-    wide = H % 256 == 0 and H >= 3072
+    wide = H % 256 == 0 and H >= 1024
     tiles = (H // 256) * 2 if wide else H // 128
     jumps, flat = _max_jumps(z, tiles)
     assert jumps > 0 and flat > 0, (jumps, flat)
