@@ -116,14 +116,14 @@ __device__ __forceinline__ float frag_bf16(const u32x4 (&w)[2], int reg) {
 
 // Accumulator element (mb, nb, reg) of lane `lane` in wave (wm, wn) sits at
 // tile row wm*64 + mb*32 + acc_row(reg, lane), tile column wn*128 + nb*32 + lane%32.
+// One output tile: workgroup b of the problem's grid, K piece kz, stages in lds.
 template <int FA, int FB>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
+__device__ __forceinline__ void gemm_block(const GemmArgs& p, int b, int kz, char* lds) {
   using G = TileGemm<256, 256, 4, 2, 0, FA, FB, true>;
-  __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
   int tm, tn;
-  if (!gemm_tile(blockIdx.x, p, tm, tn)) return;  // uniform across the workgroup
+  if (!gemm_tile(b, p, tm, tn)) return;  // uniform across the workgroup
   const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
-  const int64_t k0 = (int64_t)blockIdx.y * p.kchunk;
+  const int64_t k0 = (int64_t)kz * p.kchunk;
   const Operand oa = gemm_operand<FA>(p.A, p.a_bytes, p.a_ld, m0, k0);
   const Operand ob = gemm_operand<FB>(p.B, p.b_bytes, p.b_ld, n0, k0);
   f32x16 acc[2][4];
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
   const float alpha = p.alpha;
 
   if (p.epi == kEpiStoreF32 || p.epi == kEpiAccF32) {
-    float* base = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.c_split + m0 * p.ldc + n0;
+    float* base = static_cast<float*>(p.C) + (int64_t)kz * p.c_split + m0 * p.ldc + n0;
     const rsrc_t rs = make_rsrc(base, (uint64_t)((int64_t)(rl - 1) * ldc + cl) * 4);
     const bool accum = p.epi == kEpiAccF32;
     // The accumulate loads the 16 old values of a 32x32 block before its
@@ -316,6 +316,57 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
       }
     }
   }
+}
+
+constexpr int kGemmLds = TileGemm<256, 256, 4, 2, 0, 0, 0, true>::LDS_BYTES;
+static_assert(TileGemm<256, 256, 4, 2, 0, 0, 2, true>::LDS_BYTES == kGemmLds &&
+                  TileGemm<256, 256, 4, 2, 0, 2, 2, true>::LDS_BYTES == kGemmLds,
+              "one LDS size for every operand form");
+
+template <int FA, int FB>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+  gemm_block<FA, FB>(p, blockIdx.x, blockIdx.y, lds);
+}
+
+// Several independent GEMMs (no K split) in one grid: workgroups
+// start[i] .. start[i+1] - 1 are problem i's grid (each start a multiple of 8,
+// so that a workgroup's XCD is the same in both numberings).  Workgroups are
+// dispatched in index order as CUs free up, so the problems' tiles pack the
+// chip instead of each problem's last partial wave idling part of it.
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_group(GemmGroup q) {
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+  int i = 0;
+  while (i + 1 < q.n && (int)blockIdx.x >= q.start[i + 1]) ++i;
+  const GemmArgs& p = q.g[i];
+  const int b = (int)blockIdx.x - q.start[i];
+  if (p.a_form == 0 && p.b_form == 0) gemm_block<0, 0>(p, b, 0, lds);
+  else if (p.a_form == 0 && p.b_form == 2) gemm_block<0, 2>(p, b, 0, lds);
+  else gemm_block<2, 2>(p, b, 0, lds);
+}
+
+hipError_t launch_gemm_group(const GemmArgs* g, int n, hipStream_t st) {
+  if (n < 1 || n > kGemmGroupMax) return hipErrorInvalidValue;
+  GemmGroup q = {};
+  q.n = 0;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const GemmArgs& a = g[i];
+    if (a.M <= 0 || a.N <= 0) continue;
+    if (a.ksplit != 1 || a.kchunk % 64 != 0) return hipErrorInvalidValue;
+    const bool known = (a.a_form == 0 && (a.b_form == 0 || a.b_form == 2)) || (a.a_form == 2 && a.b_form == 2);
+    if (!known) return hipErrorInvalidValue;
+    q.g[q.n] = a;
+    q.start[q.n] = (int)blocks;
+    int64_t b = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+    b = (b + 7) / 8 * 8;  // a multiple of 8 (XCD shares when patch_m > 0, alignment of the next start)
+    blocks += b;
+    ++q.n;
+  }
+  if (q.n == 0) return hipSuccess;
+  q.start[q.n] = (int)blocks;
+  hipLaunchKernelGGL(k_gemm_group, dim3((unsigned)blocks), dim3(kGemmThreads), 0, st, q);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {

@@ -159,6 +159,17 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
+// Up to kGemmGroupMax independent GEMMs (ksplit 1, any instantiated operand
+// forms and epilogues) in one launch, their tiles packed onto the chip in the
+// order given (put the problems with the longest K first).
+constexpr int kGemmGroupMax = 3;
+struct GemmGroup {
+  GemmArgs g[kGemmGroupMax];
+  int start[kGemmGroupMax + 1];
+  int n;
+};
+hipError_t launch_gemm_group(const GemmArgs* g, int n, hipStream_t st);
+
 hipError_t launch_count_labels(const int64_t* labels, int64_t L, int64_t V, int64_t ignore_index, WsHeader* hdr,
                                int saved, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, float* loss_out, float* lse_out, hipStream_t st);

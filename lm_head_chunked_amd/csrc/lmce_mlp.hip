@@ -250,7 +250,6 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     xg.C = dx_out + r0 * H;
     xg.ldc = H;
     xg.patch_m = 4;
-    if (launch_gemm(xg, s) != hipSuccess) return LMCE_ERR_HIP;
     // weight gradients, K = the chunk's rows, both operands read MN-major
     GemmArgs wd = {};
     set_a_mnmajor(wd, dy16 + r0 * H, rows, H);
@@ -264,7 +263,6 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     wd.C = dWd_out;
     wd.ldc = I;
     wd.patch_m = 4;
-    if (launch_gemm(wd, s) != hipSuccess) return LMCE_ERR_HIP;
     GemmArgs wg = {};
     set_a_mnmajor(wg, dgu, rows, 2 * I);
     set_b_mnmajor(wg, x16 + r0 * H, rows, H);
@@ -278,7 +276,10 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     wg.C2 = dWu_out;
     wg.ldc = H;
     wg.patch_m = 4;
-    if (launch_gemm(wg, s) != hipSuccess) return LMCE_ERR_HIP;
+    // the three are independent: one grid, the longest K first, so that their
+    // tiles pack the CUs instead of each leaving a partial last wave
+    const GemmArgs three[3] = {xg, wg, wd};
+    if (launch_gemm_group(three, 3, s) != hipSuccess) return LMCE_ERR_HIP;
   }
   return LMCE_OK;
 }
