@@ -26,6 +26,10 @@
 //   dx_c = dg_c Wg + du_c Wu          (one GEMM over the packed 2I, read MN-major)
 //   dWd += dy_c^T p_c, dWg += dg_c^T x_c, dWu += du_c^T x_c   (GEMMs over the chunk's rows, both
 //                                                               operands read MN-major)
+// Independent GEMMs share one grid (launch_gemm_group), so that their tiles
+// pack the CUs instead of each leaving a partial last wave: in the forward
+// chunk c's down GEMM with chunk c+1's gate/up GEMM (p alternates between two
+// areas), in the backward dx_c with the three weight-gradient GEMMs.
 
 #include "lmce_device.h"
 #include "lmce_internal.h"
@@ -114,11 +118,11 @@ void set_b_mnmajor(GemmArgs& g, const void* p, int64_t k_rows, int64_t ld_elems)
   g.b_form = 2;
 }
 
-// p_c = silu(g) * u of rows [r0, r0 + rows) into the act area; with
-// store_gu, the bf16 gate/up values themselves into the gu area instead, in
-// the GEMM's fragment order.
-hipError_t gate_up(const MlpPlan& p, const void* x, const uint16_t* Wgu, int64_t r0, int64_t rows, void* ws,
-                   bool store_gu, hipStream_t s) {
+// The gate/up GEMM of rows [r0, r0 + rows): p_c = silu(g) * u into `act`
+// (rows x I, row-major); with store_gu, the bf16 gate/up values themselves
+// into the gu area instead, in the GEMM's fragment order.
+GemmArgs gate_up_args(const MlpPlan& p, const void* x, const uint16_t* Wgu, int64_t r0, int64_t rows, void* ws,
+                      bool store_gu, uint16_t* act) {
   GemmArgs g = {};
   set_a_kmajor(g, static_cast<const uint16_t*>(x) + r0 * p.H, rows, p.H);
   set_b_kmajor(g, Wgu, 2 * p.I, p.H);
@@ -132,11 +136,11 @@ hipError_t gate_up(const MlpPlan& p, const void* x, const uint16_t* Wgu, int64_t
     g.C = at<uint16_t>(ws, p.off_gu);
   } else {
     g.epi = kEpiSwigluFwd;
-    g.C = at<uint16_t>(ws, p.off_act);
+    g.C = act;
     g.ldc = p.I;
   }
   g.patch_m = 4;
-  return launch_gemm(g, s);
+  return g;
 }
 
 // Packs Wg and Wu into the interleaved [2I][H] matrix.
@@ -173,22 +177,34 @@ extern "C" int lmce_mlp_fwd(const void* x, const void* Wg, const void* Wu, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (pack_weights(p, Wg, Wu, workspace, s) != hipSuccess) return LMCE_ERR_HIP;
   const uint16_t* Wgu = at<uint16_t>(workspace, p.off_Wgu);
-  for (int64_t r0 = 0; r0 < L; r0 += p.cr) {
+  // p of consecutive chunks alternates between the act area and the gu area
+  // (unused by the forward), so that each chunk's down GEMM runs in one grid
+  // with the next chunk's gate/up GEMM
+  uint16_t* const act_buf[2] = {at<uint16_t>(workspace, p.off_act), at<uint16_t>(workspace, p.off_gu)};
+  int64_t rows0 = L < p.cr ? L : p.cr;
+  if (launch_gemm(gate_up_args(p, x, Wgu, 0, rows0, workspace, false, act_buf[0]), s) != hipSuccess)
+    return LMCE_ERR_HIP;
+  for (int64_t r0 = 0, c = 0; r0 < L; r0 += p.cr, ++c) {
     const int64_t rows = (L - r0) < p.cr ? (L - r0) : p.cr;
-    if (gate_up(p, x, Wgu, r0, rows, workspace, false, s) != hipSuccess) return LMCE_ERR_HIP;
-    GemmArgs g = {};
-    set_a_kmajor(g, at<uint16_t>(workspace, p.off_act), rows, I);
-    set_b_kmajor(g, Wd, H, I);
-    g.M = rows;
-    g.N = H;
-    g.kchunk = I;
-    g.ksplit = 1;
-    g.epi = kEpiStoreF32;
-    g.alpha = 1.f;
-    g.C = y_out + r0 * H;
-    g.ldc = H;
-    g.patch_m = 4;
-    if (launch_gemm(g, s) != hipSuccess) return LMCE_ERR_HIP;
+    GemmArgs g[2] = {};
+    set_a_kmajor(g[0], act_buf[c & 1], rows, I);
+    set_b_kmajor(g[0], Wd, H, I);
+    g[0].M = rows;
+    g[0].N = H;
+    g[0].kchunk = I;
+    g[0].ksplit = 1;
+    g[0].epi = kEpiStoreF32;
+    g[0].alpha = 1.f;
+    g[0].C = y_out + r0 * H;
+    g[0].ldc = H;
+    g[0].patch_m = 4;
+    int n = 1;
+    const int64_t r1 = r0 + p.cr;
+    if (r1 < L) {
+      const int64_t rows1 = (L - r1) < p.cr ? (L - r1) : p.cr;
+      g[n++] = gate_up_args(p, x, Wgu, r1, rows1, workspace, false, act_buf[(c + 1) & 1]);
+    }
+    if (launch_gemm_group(g, n, s) != hipSuccess) return LMCE_ERR_HIP;
   }
   return LMCE_OK;
 }
@@ -221,7 +237,8 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
   for (int64_t r0 = 0; r0 < L; r0 += p.cr) {
     const int64_t rows = (L - r0) < p.cr ? (L - r0) : p.cr;
     const int64_t rk = (rows + 63) / 64 * 64;  // K of the weight-gradient GEMMs (rows past `rows` read as zero)
-    if (gate_up(p, x, Wgu, r0, rows, workspace, true, s) != hipSuccess) return LMCE_ERR_HIP;
+    if (launch_gemm(gate_up_args(p, x, Wgu, r0, rows, workspace, true, nullptr), s) != hipSuccess)
+      return LMCE_ERR_HIP;
     // dp = dy_c Wd (B = Wd read MN-major, K = H), epilogue: dg, du (packed like gu) and p
     GemmArgs d = {};
     set_a_kmajor(d, dy16 + r0 * H, rows, H);
@@ -277,7 +294,8 @@ extern "C" int lmce_mlp_bwd(const void* x, const void* Wg, const void* Wu, const
     wg.ldc = H;
     wg.patch_m = 4;
     // the three are independent: one grid, the longest K first, so that their
-    // tiles pack the CUs instead of each leaving a partial last wave
+    // tiles pack the CUs instead of each leaving a partial last wave (adding
+    // the next chunk's gate/up recompute to the grid gained nothing)
     const GemmArgs three[3] = {xg, wg, wd};
     if (launch_gemm_group(three, 3, s) != hipSuccess) return LMCE_ERR_HIP;
   }
