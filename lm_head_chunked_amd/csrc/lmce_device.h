@@ -361,10 +361,13 @@ struct TileGemm {
     const int wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
     const int nk = K / BK;
-    // Every earlier reader of this LDS is past this barrier, every earlier
-    // LDS write of the workgroup has landed, and no earlier vector memory
-    // operation of this wave is still counted in vmcnt.
-    wait_vmcnt<0>();
+    // Every earlier reader of this LDS is past this barrier, and every
+    // earlier LDS write of the workgroup has landed (an earlier GEMM's DMA
+    // was waited for in its own last step).  Earlier stores of the wave (an
+    // exchange tile, a parked accumulator) may still be in flight: they count
+    // in vmcnt ahead of the stage loads, so the stage waits below cover them
+    // too (loads complete in order, stores only ever add to the count), and
+    // they drain while the first stages load instead of before.
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     raw_barrier();
     Operand aa = a, bb = b;  // gathered forms: this lane's row offsets
@@ -517,8 +520,8 @@ struct TileGemm {
     const int lane = lane_id(), wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
     const int nk = K / BK;
-    // as in run_staged(): earlier readers of this LDS are past the barrier
-    wait_vmcnt<0>();
+    // as in run_staged(): earlier readers of this LDS are past the barrier,
+    // earlier stores may still drain
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     raw_barrier();
     if (nk <= 0) return;
