@@ -264,7 +264,7 @@ def bench_mlp(args):
                    "peak_frac_bf16": tflops / PEAK_BF16_TFLOPS, "flops_per_step": 22 * lhi,
                    "call_ms": {c[0]: t for c, t in zip(calls, call_ms)}, "workspace_bytes": ws_bytes,
                    "untiled_intermediates_bytes": untiled, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm", "call": calls[dom][0], "achieved": dom_tflops,
+        "roofline": {"bound": "mfma", "kernel": "k_gemm + k_gemm_group (whole call)", "call": calls[dom][0], "achieved": dom_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
                      "traffic": None, "mean_ms": call_ms[dom]},
         "cpu_baseline": None,
