@@ -246,10 +246,11 @@ int lmce_chunked_bwd(const void* h, const void* W, const int64_t* labels,
  * keeps nothing of them) and takes no forward state: it may run on its own.
  * Limits: 128 <= H <= 16384 with H % 128 == 0, 64 <= I <= 65536 with
  * I % 64 == 0, 1 <= L <= 2^24, 1 <= chunk_rows <= 65536, and 4 I H and
- * 4 I ceil(chunk_rows / 128) 128 at most 2^31 - 4096 (LMCE_ERR_UNSUPPORTED
- * otherwise).  The workspace holds the packed weights and their transposes
- * (5 I H bf16) and one chunk's intermediates; lmce_mlp_workspace_size gives
- * its size.  Pointer rules as above; there is no asynchronous status.
+ * 4 I ceil(c / 64) 64 at most 2^31 - 4096, c = min(chunk_rows, L)
+ * (LMCE_ERR_UNSUPPORTED otherwise).  The workspace holds the packed gate/up
+ * weights (2 I H bf16) and one chunk's intermediates (its gate/up values, p
+ * and their gradients); lmce_mlp_workspace_size gives its size.  Pointer
+ * rules as above; there is no asynchronous status.
  */
 int lmce_mlp_workspace_size(int64_t L, int64_t H, int64_t I, int64_t chunk_rows, size_t* bytes);
 int lmce_mlp_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd,
