@@ -77,14 +77,14 @@ const char* lmce_strerror(int status);
 /*
  * Bytes of device workspace that lmce_fwd / lmce_bwd and the training pair
  * need for this shape: per-row partials and orders (O(L) words), a fixed
- * exchange ring for the group passes (at most 128 MiB), for H >= 1024 a
- * parking area for their accumulators (at most 64 MiB), and the dW pass's
- * partial slices (at most 64 MiB).  h and W are read in place, never copied
- * or transposed; the passes that skip unlabelled rows read h's rows through
- * their order, except where H < 1024 or H % 256 != 0 or L * H * 2 > 2^31
- * bytes: there the workspace also holds a gathered bf16 copy of those rows
- * (L * H * 2 bytes).  It never holds an L x V array.  Writes the size to
- * *bytes.  Returns LMCE_OK or a shape error.
+ * exchange ring for the group passes (at most 128 MiB), where H % 256 == 0
+ * and H >= 1024 a parking area for their accumulators (at most 64 MiB), and
+ * the dW pass's partial slices (at most 64 MiB).  h and W are read in place,
+ * never copied or transposed; the passes that skip unlabelled rows read h's
+ * rows through their order, except where H < 1024 or H % 256 != 0 or
+ * L * H * 2 > 2^31 bytes: there the workspace also holds a gathered bf16
+ * copy of those rows (L * H * 2 bytes).  It never holds an L x V array.
+ * Writes the size to *bytes.  Returns LMCE_OK or a shape error.
  */
 int lmce_workspace_size(int64_t L, int64_t H, int64_t V, int64_t chunk_rows, size_t* bytes);
 

@@ -70,12 +70,12 @@ struct BwdArgs {
   const float* lse;
   const float* grad_loss;
   int64_t L, H, V, ignore_index;
-  int group_size;       // workgroups per group = H / HS (HS = 256 if H % 256 == 0, else 128)
+  int group_size;       // workgroups per group = H / HS (HS = 256 if H % 256 == 0 and H >= 1024, else 128)
   int n_groups;
   int xcd_members;      // > 0: members of one group per XCD (xcd_tiled order); 0: the pass's default order
   int spin_limit;       // bound of every group wait
   unsigned* sync;       // [n_groups * kSyncStride] arrival counters, zeroed before the launch
-  uint16_t* xbuf;       // [n_groups][2][2 * group_size][256][128] exchange slots
+  uint16_t* xbuf;       // [n_groups][2][2 * R * group_size][256][128] exchange slots, R = round_tiles(HS)
   float* park;          // [workgroups][256 x 256] parked accumulators (HS = 256 only)
   float* xstat;         // [n_groups][3][group_size][256] round maxima (2 slots) and final sums, fused forward
   float* O;             // [L][H] normalised sum_v softmax(z)_v W_v by row: the fused forward's output, written into
@@ -110,13 +110,13 @@ struct BwdArgs {
 };
 
 // ------------------------------------------------------------------ GEMM
-// C = alpha * A B^T on the tile engine: A has M rows, B has N rows, both bf16
-// with K contiguous, either linear (row r, K index k at r * ld + 2k bytes) or
-// K-tiled as the transposer writes them ((k / 128) * tstride + r * ld +
-// 2 (k % 128)).  256 x 256 output tiles; grid.y splits K into ksplit pieces
-// of kchunk (a multiple of 64, of 128 for a K-tiled operand), piece z writing
-// at C + z * c_split (elements).  Rows past M or N read as zero and are not
-// written; K past an operand's end reads as zero.
+// C = alpha * A B^T on the tile engine: A has M rows, B has N rows, both bf16,
+// each read in place either K-major (row r, K index k at r * ld + 2k bytes)
+// or MN-major (at k * ld + 2r: a row-major [K][rows] matrix used as the
+// transposed operand).  256 x 256 output tiles; grid.y splits K into ksplit
+// pieces of kchunk (a multiple of 64), piece z writing at C + z * c_split
+// (elements).  Rows past M or N read as zero and are not written; K past an
+// operand's end reads as zero.
 enum GemmEpi {
   kEpiStoreF32 = 0,   // C fp32 [M][ldc] = alpha * acc
   kEpiAccF32 = 1,     // C fp32 [M][ldc] += alpha * acc
