@@ -137,12 +137,14 @@ int lmce_fwd_noalloc(const void* h, const void* W, const int64_t* labels,
 /*
  * Backward.  Same page and sections; the gradient of the mean NLL is
  * G = g/N * valid * (softmax - onehot).  Each logit tile is recomputed from
- * h and W, turned into bf16 G and contracted in the same round into
- *   dh_out fp32 [L, H] = G W     (overwritten, not accumulated)
- *   dW_out fp32 [V, H] = G^T h   (overwritten, not accumulated)
+ * h and W, turned into bf16 G' = valid * (softmax - onehot) and contracted
+ * in the same round into
+ *   dh_out fp32 [L, H] = g/N * G' W     (overwritten, not accumulated)
+ *   dW_out fp32 [V, H] = g/N * G'^T h   (overwritten, not accumulated)
  * by the co-resident workgroups that own the 128- or 256-wide H slices of
- * the outputs; a G tile lives only in the workspace's exchange ring for the
- * one round that consumes it.  The device must support cooperative launches
+ * the outputs; g/N multiplies the fp32 results, so that its own rounding
+ * does not scale every term alike, and a G' tile lives only in the
+ * workspace's exchange ring for the one round that consumes it.  The device must support cooperative launches
  * (otherwise LMCE_ERR_HIP or LMCE_ERR_UNSUPPORTED).
  *
  *   lse        fp32 [L]  the lse_out of lmce_fwd on the same inputs

@@ -342,7 +342,8 @@ int launch_group_pass(int pass, BwdArgs& a, const Plan& p, int64_t items, hipStr
   a.xcd_members = group_xcd_members(pass, hs, group_size, (int)groups * group_size);
   if (launch_zero_u32(a.sync, (int)groups * kSyncStride, s) != hipSuccess) return LMCE_ERR_HIP;
   if (launch_bwd_group(pass, a, hs, (int)groups * group_size, s) != hipSuccess) return LMCE_ERR_HIP;
-  if (pass == kPassDw && launch_dw_tail(a, hs, s) != hipSuccess) return LMCE_ERR_HIP;
+  if (pass == kPassDw && (launch_dw_tail(a, hs, s) != hipSuccess || launch_dw_scale(a, hs, s) != hipSuccess))
+    return LMCE_ERR_HIP;
   return LMCE_OK;
 }
 

@@ -10,9 +10,12 @@
 // accumulator (HS = 128 in registers, or 256 parked in the workspace between
 // rounds).  In every round each member recomputes R = round_tiles(HS) full-H
 // 256 x 256 logit tiles with MFMA (two with 256-wide slices, one with
-// 128-wide), turns each into bf16 G (or P) in registers and writes it to the
-// group's exchange slot; after a group barrier every member contracts all
-// R x s tiles of the round into its own slice.  Each logit is thus
+// 128-wide), turns each into bf16 G' = valid * (softmax - onehot) (or P) in
+// registers and writes it to the group's exchange slot; after a group barrier
+// every member contracts all R x s tiles of the round into its own slice.
+// The factor g/N of G = g/N * G' multiplies the fp32 slice when it is stored:
+// folded into G before the bf16 rounding, its own rounding error (up to
+// 2^-9 relative, the same for every term) would scale the whole result.  Each logit is thus
 // recomputed exactly once per pass and no logit or G tile exists for more
 // than one round (the exchange holds 2 x R x s tiles per group).  Two tiles
 // per round halve the group barriers and the parked accumulator's round
@@ -207,6 +210,22 @@ __global__ __launch_bounds__(256) void k_dw_tail(const float* __restrict__ part,
   }
 }
 
+// dW *= g/N after a dW pass with 128-wide slices (which stores G'^T h).
+__global__ __launch_bounds__(256) void k_dw_scale(float* __restrict__ dW, int64_t n4, const float* __restrict__ grad_loss,
+                                                  const WsHeader* __restrict__ hdr) {
+  const int n = hdr->n_valid;
+  const float f = *grad_loss / (float)(n > 0 ? n : 1);
+  float4* d = reinterpret_cast<float4*>(dW);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4 v = d[i];
+    v.x *= f;
+    v.y *= f;
+    v.z *= f;
+    v.w *= f;
+    d[i] = v;
+  }
+}
+
 __global__ void k_zero_u32(unsigned* __restrict__ p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -368,6 +387,16 @@ __device__ __forceinline__ void gstage_flush(const char* lds, rsrc_t rslot, int 
   }
 }
 
+// g/N, the factor of G = g/N * G' that the passes apply to their fp32
+// results.  Read where a result is stored (relaxed atomic loads, which the
+// compiler does not hoist), so that it is not held in a register across the
+// rounds.
+__device__ __forceinline__ float grad_factor(const BwdArgs& p) {
+  const int n = __hip_atomic_load(&p.hdr->n_valid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float g = __hip_atomic_load(p.grad_loss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return g / (float)(n > 0 ? n : 1);
+}
+
 // ---------------------------------------------------------------- dh pass
 // Group = 256 rows of h.  Round k: member j recomputes the logit tiles of
 // vocabulary rows [((k*R + e)*s + j)*256, +256), e < R = round_tiles(HS),
@@ -383,7 +412,8 @@ __device__ __forceinline__ void gstage_flush(const char* lds, rsrc_t rslot, int 
 // past L are skipped.  ZERO writes zeros instead (acc is not read).
 template <int MB, int NB, bool ZERO>
 __device__ __forceinline__ void store_rows_perm(float* dh, const int* perm, int64_t pos0, int64_t L, int64_t H,
-                                                int64_t c0, const f32x16 (&acc)[MB][NB], int row0, int col0, int lane) {
+                                                int64_t c0, const f32x16 (&acc)[MB][NB], int row0, int col0, int lane,
+                                                float f = 1.f) {
   const int lrow = (lane >> 5) << 2;  // row offset of this lane half
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -393,7 +423,7 @@ __device__ __forceinline__ void store_rows_perm(float* dh, const int* perm, int6
       if (pos < L) {
         float* d = dh + (int64_t)perm[pos] * H + c0 + col0 + (lane & 31);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) d[nb * 32] = ZERO ? 0.f : acc[mb][nb][reg];
+        for (int nb = 0; nb < NB; ++nb) d[nb * 32] = ZERO ? 0.f : acc[mb][nb][reg] * f;
       }
     }
 }
@@ -422,8 +452,6 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
   const int vt128 = (int)((V + 127) / 128);
   const int rounds = (vt256 + R * s - 1) / (R * s);
   const int nrb = (int)((L + 255) / 256);
-  const int n_valid = p.hdr->n_valid;
-  const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
   // Rows in this pass's labelled-first order when it saves a block
   // (crow[position] = row, h rows in hp): blocks past the labelled rows only
   // write their zero dh rows, and every row is read and written through the
@@ -445,7 +473,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
       continue;
     }
     // producer wave (wm: vocabulary quarter, wn: token half); lane's 4 tokens
-    float lse2[4], scale[4];
+    float lse2[4], keep[4];
     int lab[4];  // label, or -2^30 for rows that take no gradient
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
@@ -454,7 +482,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
       const int64_t y = t < rend ? p.labels[src] : p.ignore_index;
       const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
       lab[nb] = valid ? (int)y : -(1 << 30);
-      scale[nb] = valid ? gscale : 0.f;
+      keep[nb] = valid ? 1.f : 0.f;
       lse2[nb] = t < rend ? p.lse[src] * kLog2e : INFINITY;  // rows past L: probability 0
     }
     const Operand oh = by_index ? gathered_operand(p.h, (uint64_t)L * H * 2, (uint32_t)(H * 2), p.crow + r0,
@@ -476,9 +504,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
           const Operand ow = linear_operand(p.W + (int64_t)v0 * H, (uint64_t)(V - v0) * H * 2, (uint32_t)(H * 2));
           if (by_index) PG::run(ow, oh, (int)H, lds, z);
           else P::run(ow, oh, (int)H, lds, z);
-          // G[token][v] = scale * (exp(z - lse) - [v == y]), staged in LDS as
-          // [token][v], 4 consecutive v per write.  Tile-local coordinates:
-          // vl = v - v0, the label at lab - v0.
+          // G'[token][v] = valid * (exp(z - lse) - [v == y]), staged in LDS as
+          // [token][v], 4 consecutive v per write (G = g/N * G': the factor is
+          // applied to the fp32 dh, so that its bf16 rounding does not scale
+          // every term alike).  Tile-local coordinates: vl = v - v0, the
+          // label at lab - v0.
           const int vlim = min((int)(V - v0), 256);
           raw_barrier();  // every wave is done with the GEMM's last LDS stage
   #pragma unroll
@@ -494,7 +524,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
                 for (int e = 0; e < 4; ++e) {
                   float pr = exp2_fast(__builtin_fmaf(z[mb][nb][qq * 4 + e], kLog2e, -lse2[nb]));
                   pr = (vl0 + e == yl) ? pr - 1.f : pr;
-                  gv[e] = pr * ((vl0 + e < vlim) ? scale[nb] : 0.f);
+                  gv[e] = pr * ((vl0 + e < vlim) ? keep[nb] : 0.f);
                 }
                 gstage_put(lds, wn * 128 + nb * 32 + (lane & 31), vl0, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
               }
@@ -520,15 +550,17 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
              ntl * 128, lds, dacc);
       if constexpr (kPark) park_acc(dacc, park, wave, lane);  // also after the last round: dacc is dead at the back edge
     }
-    // dh[r][c] for r < L (waves: wm token quarter, wn column half)
+    // dh[r][c] = g/N * (G' W)[r][c] for r < L (waves: wm token quarter, wn column half)
     if constexpr (kPark) {
       f32x16 fin[C::MB][C::NB];
       unpark_acc(fin, park, wave, lane);
-      if (reordered) store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, fin, wm * 64, wn * (HS / 2), lane);
-      else store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
+      if (reordered)
+        store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, fin, wm * 64, wn * (HS / 2), lane, grad_factor(p));
+      else store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane, grad_factor(p));
     } else {
-      if (reordered) store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, dacc, wm * 64, wn * (HS / 2), lane);
-      else store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane);
+      if (reordered)
+        store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, dacc, wm * 64, wn * (HS / 2), lane, grad_factor(p));
+      else store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane, grad_factor(p));
     }
   }
 }
@@ -537,10 +569,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
 // Group = 256 vocabulary rows.  Round k: member j recomputes the logit tiles
 // of tokens [((k*R + e)*s + j)*256, +256), e < R = round_tiles(HS), against the
 // group's vocabulary rows (A = h, B = W: tokens on M, vocabulary on N), forms
-// G^T[v][token] and stores each as two K-tiles (2(e*s + j), +1) of the
+// G'^T[v][token] and stores each as two K-tiles (2(e*s + j), +1) of the
 // round's slot [256 v][K].  Then
 //   dW[v rows][c0 .. c0+HS] += slot[256][K] * h[round's tokens][c0 .. c0+HS],
-// h's rows read MN-major (no copy).
+// h's rows read MN-major (no copy), and the slice is stored times g/N.
 template <int HS>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   using P = typename BwdCfg<HS>::PA;
@@ -548,7 +580,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   using C = typename BwdCfg<HS>::CH;
   constexpr bool kPark = BwdCfg<HS>::kPark;
   __shared__ __attribute__((aligned(16))) char lds[BwdCfg<HS>::kLds];
-  __shared__ float row_lse2[256], row_scale[256];
+  __shared__ float row_lse2[256], row_keep[256];  // lse * log2(e); 1 for rows that take a gradient, else 0
   __shared__ int row_lab[256];  // label - v0 of the group's vocabulary block, or -1
   __shared__ int s_flag;
 
@@ -576,8 +608,6 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   const int rt128 = (int)((L + 127) / 128);
   const int rounds = (rt256 + R * s - 1) / (R * s);
   const int nvb = (int)((V + 255) / 256);
-  const int n_valid = p.hdr->n_valid;
-  const float gscale = *p.grad_loss / (float)(n_valid > 0 ? n_valid : 1);
   unsigned epoch = 0;
 
   // Blocks g, g + n_groups, ... in lockstep with the other groups (member j of
@@ -613,7 +643,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
             const int64_t y = t < rend ? labels[t] : p.ignore_index;
             const bool valid = t < rend && y != p.ignore_index && y >= 0 && y < V;
             row_lab[threadIdx.x] = (valid && y >= v0 && y < v0 + 256) ? (int)(y - v0) : -1;
-            row_scale[threadIdx.x] = valid ? gscale : 0.f;
+            row_keep[threadIdx.x] = valid ? 1.f : 0.f;
             row_lse2[threadIdx.x] = t < rend ? lse[t] * kLog2e : INFINITY;
           }
           f32x16 z[P::MB][P::NB];
@@ -625,7 +655,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
                                                          (uint32_t)(H * 2), nullptr, (int)(rend - r0));
           if (by_index) PAG::run(oh, ow, (int)H, lds, z);
           else P::run(oh, ow, (int)H, lds, z);
-          // G^T[v][token]: lane = v (column), 4 consecutive tokens per store.
+          // G'^T[v][token]: lane = v (column), 4 consecutive tokens per store.
           // Token data is read once per 4-token group and reused for the
           // lane's 4 vocabulary columns; columns past V get a zero factor.
           const int vlim = (int)min<int64_t>(V - v0, 256);
@@ -638,12 +668,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
   #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
               const int tl0 = wm * 64 + mb * 32 + acc_row(qq * 4, lane);
-              float tlse[4], tsc[4];
+              float tlse[4], tkeep[4];
               int tlab[4];
   #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 tlse[e] = row_lse2[tl0 + e];
-                tsc[e] = row_scale[tl0 + e];
+                tkeep[e] = row_keep[tl0 + e];
                 tlab[e] = row_lab[tl0 + e];
               }
   #pragma unroll
@@ -654,7 +684,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
                 for (int e = 0; e < 4; ++e) {
                   float pr = exp2_fast(__builtin_fmaf(z[mb][nb][qq * 4 + e], kLog2e, -tlse[e]));
                   pr = (vl == tlab[e]) ? pr - 1.f : pr;
-                  gv[e] = pr * (tsc[e] * vmask[nb]);
+                  gv[e] = pr * (tkeep[e] * vmask[nb]);
                 }
                 gstage_put(lds, vl, tl0, pack_bf16x4(gv[0], gv[1], gv[2], gv[3]));
               }
@@ -694,10 +724,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) fin[mb][nb] = dacc[mb][nb];
     }
+    // dW = g/N * (G'^T h): the factor in fp32, as in the dh pass.  With
+    // 128-wide slices (accumulators held in registers across the rounds) a
+    // product here makes the compiler spill the accumulators in every round,
+    // so that variant stores G'^T h and k_dw_scale applies the factor after
+    // the pass.
+    const float f = HS == 256 ? grad_factor(p) : 1.f;
     if (to_part)
-      store_tile_f32(p.dw_part + ((int64_t)g * s + j) * 256 * HS, 256, HS, HS, fin, wm * 64, wn * (HS / 2), lane);
+      store_tile_f32(p.dw_part + ((int64_t)g * s + j) * 256 * HS, 256, HS, HS, fin, wm * 64, wn * (HS / 2), lane, f);
     else
-      store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane);
+      store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane, f);
   }
 }
 
@@ -1094,6 +1130,14 @@ hipError_t launch_dw_tail(const BwdArgs& a, int hs, hipStream_t st) {
   if (gpb < 2) return hipSuccess;  // each leftover block went whole to one group
   hipLaunchKernelGGL(k_dw_tail, dim3((unsigned)(tail_blocks * a.group_size)), dim3(256), 0, st, (const float*)a.dw_part,
                      a.dW, a.V, a.H, hs, a.group_size, gpb, (int64_t)full_waves * a.n_groups * 256);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_scale(const BwdArgs& a, int hs, hipStream_t st) {
+  if (hs == 256) return hipSuccess;  // the 256-wide pass applied the factor itself
+  const int64_t n4 = a.V * a.H / 4;  // H is a multiple of 128
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_dw_scale, dim3((unsigned)blocks), dim3(256), 0, st, a.dW, n4, a.grad_loss, a.hdr);
   return hipGetLastError();
 }
 

@@ -591,6 +591,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[MB][NB]) {
     for (int j = 0; j < NB; ++j) zero(acc[i][j]);
 }
 
+
 __device__ __forceinline__ float pick16(const f32x16& x, int reg) {
   float v = 0.f;
 #pragma unroll
@@ -640,10 +641,11 @@ __device__ __forceinline__ void store_b32(rsrc_t rs, uint32_t voff, uint32_t sof
 // `rows_left` are skipped.  Address parts that are the same for the whole
 // wave go in the scalar offset; a skipped row gets a vector offset past the
 // resource end (the range check applies to the vector offset), so its store
-// is dropped.
+// is dropped.  Each value is stored times f.
 template <int MB, int NB>
 __device__ __forceinline__ void store_tile_f32(float* base, int64_t rows_left, int64_t ld, int64_t cols_left,
-                                               const f32x16 (&acc)[MB][NB], int row0, int col0, int lane) {
+                                               const f32x16 (&acc)[MB][NB], int row0, int col0, int lane,
+                                               float f = 1.f) {
   const rsrc_t rs = make_rsrc(base, (uint64_t)((rows_left - 1) * ld + cols_left) * 4);
   lane = lane_id();
   row0 = opaque_s(row0);
@@ -658,7 +660,7 @@ __device__ __forceinline__ void store_tile_f32(float* base, int64_t rows_left, i
         const int rr = row0 + mb * 32 + ((reg >> 2) << 3) + (reg & 3);
         const uint32_t soff = (uint32_t)(((int64_t)rr * ld + col0 + nb * 32) * 4);
         const uint32_t v = (rr + lrow < rows_left) ? voff : 0xfffffff0u;
-        store_b32(rs, v, soff, acc[mb][nb][reg]);
+        store_b32(rs, v, soff, acc[mb][nb][reg] * f);
       }
 }
 

@@ -67,6 +67,7 @@ __all__ = [
     "fwd_bwd",
     "rows_forward",
     "rows_dh",
+    "cols_dW",
 ]
 
 
@@ -211,3 +212,33 @@ def rows_dh(h_rows, W, labels_rows, n_valid, ignore_index=-100, grad=1.0):
         return np.zeros_like(h64)
     return (P * (float(grad) / n_valid)) @ W64
 
+
+def cols_dW(h, W_cols, labels, cols, lse, V, ignore_index=-100, grad=1.0, block_rows=8192):
+    """Rows `cols` of dW (the given vocabulary entries), from every row's lse.
+
+    dW_v = sum_i G_iv h_i, G_iv = (grad / N) * valid_i * (exp(z_iv - lse_i) - [v == y_i]):
+    column v of G needs z_iv = W_v . h_i for every row i and that row's lse
+    (forward() gives it), so a few vocabulary entries can be checked where the
+    whole dW would be too slow.  W_cols holds the rows of W at `cols`; V is the
+    vocabulary size, for the label check.  h is widened block by block.
+    """
+    W64 = _widen(W_cols, "W_cols")
+    cols = np.asarray(cols).astype(np.int64, copy=False)
+    if W64.shape[0] != cols.shape[0] or np.any((cols < 0) | (cols >= V)):
+        raise ValueError("cols must index W's rows, one per row of W_cols")
+    y, valid = _check_labels(labels, V, ignore_index)
+    lse = np.asarray(lse, dtype=np.float64)
+    L = y.shape[0]
+    n_valid = int(valid.sum())
+    dW = np.zeros((cols.shape[0], W64.shape[1]), dtype=np.float64)
+    if n_valid == 0:
+        return dW
+    scale = float(grad) / float(n_valid)
+    for r0 in range(0, L, block_rows):
+        r1 = min(L, r0 + block_rows)
+        h64 = _widen(h[r0:r1], "h")
+        Gc = np.exp(h64 @ W64.T - lse[r0:r1, None])
+        Gc -= (y[r0:r1, None] == cols[None, :])
+        Gc[~valid[r0:r1], :] = 0.0
+        dW += (Gc * scale).T @ h64
+    return dW

@@ -266,7 +266,8 @@ def pin_label_range(orc):
         yb[4] = bad
         for call in (lambda: orc.forward(h, W, yb), lambda: orc.backward(h, W, yb),
                      lambda: orc.fwd_bwd(h, W, yb), lambda: orc.rows_forward(h, W, yb),
-                     lambda: orc.rows_dh(h, W, yb, 5)):
+                     lambda: orc.rows_dh(h, W, yb, 5),
+                     lambda: orc.cols_dW(h, W[:2], yb, [0, 1], np.zeros(L), V)):
             try:
                 call()
             except ValueError:
@@ -296,6 +297,29 @@ def pin_row_helpers(orc):
     assert np.max(np.abs(dh - out["dh"][rows])) <= 1e-12
 
 
+def pin_col_helper(orc):
+    """cols_dW agrees with the full dW entry by entry: vocabulary entries that
+    are the label of one or several rows, of an ignored row only, and of none,
+    including the first and the last; blocks of rows that split the rows
+    unevenly do not change it."""
+    L, H, V = 37, 12, 50
+    h, W, y = _case(L, H, V, seed=17, ignore=(3, 4, 30))
+    y[[5, 6, 7]] = 11  # a label shared by three rows
+    y[8] = V - 1
+    y[9] = 0
+    y[3] = -100
+    out = orc.fwd_bwd(h, W, y, grad=0.75)
+    never = [v for v in range(V) if v not in set(y.tolist())]
+    cols = np.array([0, 11, V - 1, int(y[10]), never[0]])
+    for block in (5, 8192):
+        dW = orc.cols_dW(h, W[cols], y, cols, out["lse"], V, grad=0.75, block_rows=block)
+        ref = out["dW"][cols]
+        assert np.max(np.abs(dW - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+    # no labelled row: zero
+    yi = np.full(L, -100)
+    assert not orc.cols_dW(h, W[cols], yi, cols, out["lse"], V).any()
+
+
 ALL_PINS = [
     pin_zero_weights,
     pin_bruteforce_decimal,
@@ -307,4 +331,5 @@ ALL_PINS = [
     pin_statistics,
     pin_label_range,
     pin_row_helpers,
+    pin_col_helper,
 ]

@@ -12,6 +12,10 @@ at full size, against values that only the fp64 CPU oracle computed:
   * dh on 512 sampled rows (row 0, the last row, ignored rows, random rows)
     against the oracle's rows_dh, computed here (relative Frobenius <= 1e-2;
     ignored rows exactly 0);
+  * 24 sampled rows of dW (vocabulary entries 0, 1, 2 and V - 1, the labels
+    of a few rows, random entries) against the oracle's cols_dW over all L
+    rows, fed the oracle's full-length lse from the golden file (relative
+    Frobenius <= 1e-2);
   * sum over the vocabulary of dW is ~0 (softmax minus one-hot sums to 0);
 and a reduced instance (the first 1024 rows at full H and V) is compared with
 the full oracle on every output, dW included.
@@ -105,6 +109,16 @@ def test_full_size_against_full_oracle(name, train):
     assert e_dh <= GRAD_REL
     ignored = (y_c[rows] == -100).numpy()
     assert np.all(dh_gpu[ignored] == 0.0)
+
+    gv = torch.Generator().manual_seed(321)
+    cols = torch.cat([torch.tensor([0, 1, 2, wl.V - 1]), y_c[y_c != -100][:4],
+                      torch.randperm(wl.V, generator=gv)[:24]])
+    cols = torch.unique(cols)[:24]
+    dW_ref = oracle.cols_dW(np32(h_c), np32(W_c[cols]), y_c.numpy(), cols.numpy(), lse_ref, wl.V)
+    dW_gpu = dW[cols.to(dev)].cpu().numpy()
+    e_dW = rel_fro(dW_gpu, dW_ref)
+    say(f"[{name}] dW rel err on {len(cols)} sampled vocabulary rows over all {wl.L} rows {e_dW:.2e}")
+    assert e_dW <= GRAD_REL
 
     colsum = dW.double().sum(0)
     ratio = float(colsum.norm() / dW.double().norm())

@@ -33,6 +33,10 @@ MUTATIONS = {
     "label_range_drops_negative": ("bad = valid & ((y < 0) | (y >= V))", "bad = valid & (y >= V)"),
     "label_range_off_by_one_at_V": ("bad = valid & ((y < 0) | (y >= V))", "bad = valid & ((y < 0) | (y > V))"),
     "label_range_check_removed": ("    if np.any(bad):\n", "    if False:\n"),
+    "cols_dW_grad_ignored": ("scale = float(grad) / float(n_valid)", "scale = 1.0 / float(n_valid)"),
+    "cols_dW_onehot_dropped": ("        Gc -= (y[r0:r1, None] == cols[None, :])\n", ""),
+    "cols_dW_ignored_rows_kept": ("        Gc[~valid[r0:r1], :] = 0.0\n", ""),
+    "cols_dW_first_block_only": ("        dW += (Gc * scale).T @ h64\n", "        dW += (Gc * scale).T @ h64 if r0 == 0 else 0.0\n"),
 }
 
 
