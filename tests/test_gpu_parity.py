@@ -569,3 +569,45 @@ def test_label_error_accumulates_until_read():
     assert math.isnan(float(loss_bad)) and math.isfinite(float(loss))
     assert torch.isfinite(dh).all() and torch.isfinite(dW).all()
     assert lm.lmce_read_status(ws) == _lib.LMCE_OK
+
+
+@pytest.mark.parametrize("train", [False, True], ids=["plain", "train"])
+def test_row_shards_compose_to_the_whole(train):
+    """How the loss splits over GPUs by rows, on one GPU: each row shard runs
+    on its own with the upstream gradient g * N_shard / N (so that its
+    g / N_shard is the whole's g / N); the shards' dh rows are the whole's,
+    their dW summed is the whole's dW, and the N-weighted mean of their
+    losses is the whole's loss.  Checked against the oracle on the whole and,
+    tighter, against one GPU call on the whole.  Unequal shards, one with few
+    labels, and a 256-wide slice (H = 1024)."""
+    L, H, V = 1500, 1024, 3000
+    say(f"[case] row shards L={L} H={H} V={V} train={train}")
+    h, W, y = synth.random_case(L, H, V, seed=34, w_std=0.05, ignore_frac=0.1)
+    y[900:1340] = -100  # the second shard keeps few labels
+    bounds = [(0, 700), (700, 1400), (1400, L)]
+    dev = torch.device("cuda:0")
+    hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
+    g = 0.75
+    n_total = (yd != -100).sum()  # on the device, as a sharded run would all-reduce it
+    dh_parts, dW_sum, loss_sum = [], None, torch.zeros((), dtype=torch.float32, device=dev)
+    for r0, r1 in bounds:
+        n_s = (yd[r0:r1] != -100).sum()
+        g_s = (g * n_s.float() / n_total.float()).reshape(())
+        ws = torch.empty(lm.lmce_workspace_size(r1 - r0, H, V), dtype=torch.uint8, device=dev)
+        loss, _, dh, dW = run_pair(train, hd[r0:r1].contiguous(), Wd, yd[r0:r1].contiguous(), -100, 256, ws, g_s)
+        assert lm.lmce_read_status(ws) == _lib.LMCE_OK
+        dh_parts.append(dh)
+        dW_sum = dW.clone() if dW_sum is None else dW_sum + dW
+        loss_sum = loss_sum + loss * n_s.float()
+    loss_c = float(loss_sum / n_total.float())
+    dh_c = torch.cat(dh_parts).cpu().numpy()
+    dW_c = dW_sum.cpu().numpy()
+    whole = run_gpu(h, W, y, grad=g, train=train)
+    ref = oracle.fwd_bwd(np32(h), np32(W), y.numpy(), grad=g)
+    e_ref = (abs(loss_c - ref["loss"]) / abs(ref["loss"]), rel_fro(dh_c, ref["dh"]), rel_fro(dW_c, ref["dW"]))
+    e_gpu = (abs(loss_c - whole["loss"]) / abs(whole["loss"]), rel_fro(dh_c, whole["dh"]), rel_fro(dW_c, whole["dW"]))
+    say(f"[shards] vs oracle: loss {e_ref[0]:.2e} dh {e_ref[1]:.2e} dW {e_ref[2]:.2e}; "
+        f"vs one call: loss {e_gpu[0]:.2e} dh {e_gpu[1]:.2e} dW {e_gpu[2]:.2e}")
+    assert e_ref[0] <= LOSS_REL and e_ref[1] <= GRAD_REL and e_ref[2] <= GRAD_REL
+    assert e_gpu[0] <= 1e-5 and e_gpu[1] <= 1e-5 and e_gpu[2] <= 1e-5
+    assert np.all(dh_c[(y == -100).numpy()] == 0.0)
