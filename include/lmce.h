@@ -210,8 +210,8 @@ int lmce_bwd_train(const void* h, const void* W, const int64_t* labels, const fl
  * back, and dW is accumulated in memory once per chunk.
  *
  *   lmce_chunked_workspace_size: bytes for this shape: the chunk's logits,
- *     its bf16 G and G^T, a K-tiled copy of W^T, dh partials of the chunk,
- *     per-row nll (O(L) floats).
+ *     its bf16 G, dh partials of the chunk, per-row nll (O(L) floats); W and
+ *     the chunk's rows of h are read in place.
  *   lmce_chunked_fwd: loss_out and lse_out as lmce_fwd.
  *   lmce_chunked_bwd: dh_out and dW_out as lmce_bwd (overwritten); it
  *     recomputes every chunk's logits and their lse, as autograd over a
