@@ -14,10 +14,11 @@
 // registers and writes it to the group's exchange slot; after a group barrier
 // every member contracts all R x s tiles of the round into its own slice.
 // The factor g/N of G = g/N * G' multiplies the fp32 slice when it is stored:
-// folded into G before the bf16 rounding, its own rounding error (up to
-// 2^-9 relative, the same for every term) would scale the whole result.  Each logit is thus
-// recomputed exactly once per pass and no logit or G tile exists for more
-// than one round (the exchange holds 2 x R x s tiles per group).  Two tiles
+// folded into G before the bf16 rounding, its own rounding error (up to 2^-9
+// relative, the same for every term) would scale the whole result.  Each
+// logit is thus recomputed exactly once per pass and no logit or G tile
+// exists for more than one round (the exchange holds 2 x R x s tiles per
+// group).  Two tiles
 // per round halve the group barriers and the parked accumulator's round
 // trips; four were slower (the exchange then outgrows what the last-level
 // cache keeps).
@@ -211,8 +212,8 @@ __global__ __launch_bounds__(256) void k_dw_tail(const float* __restrict__ part,
 }
 
 // dW *= g/N after a dW pass with 128-wide slices (which stores G'^T h).
-__global__ __launch_bounds__(256) void k_dw_scale(float* __restrict__ dW, int64_t n4, const float* __restrict__ grad_loss,
-                                                  const WsHeader* __restrict__ hdr) {
+__global__ __launch_bounds__(256) void k_dw_scale(float* __restrict__ dW, int64_t n4,
+                                                  const float* __restrict__ grad_loss, const WsHeader* __restrict__ hdr) {
   const int n = hdr->n_valid;
   const float f = *grad_loss / (float)(n > 0 ? n : 1);
   float4* d = reinterpret_cast<float4*>(dW);
@@ -555,11 +556,13 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh(BwdArgs p) {
       f32x16 fin[C::MB][C::NB];
       unpark_acc(fin, park, wave, lane);
       if (reordered)
-        store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, fin, wm * 64, wn * (HS / 2), lane, grad_factor(p));
+        store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, fin, wm * 64, wn * (HS / 2), lane,
+                                             grad_factor(p));
       else store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane, grad_factor(p));
     } else {
       if (reordered)
-        store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, dacc, wm * 64, wn * (HS / 2), lane, grad_factor(p));
+        store_rows_perm<C::MB, C::NB, false>(p.dh, p.crow, r0, L, H, c0, dacc, wm * 64, wn * (HS / 2), lane,
+                                             grad_factor(p));
       else store_tile_f32(p.dh + r0 * H + c0, L - r0, H, H - c0, dacc, wm * 64, wn * (HS / 2), lane, grad_factor(p));
     }
   }
@@ -731,7 +734,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dW(BwdArgs p) {
     // the pass.
     const float f = HS == 256 ? grad_factor(p) : 1.f;
     if (to_part)
-      store_tile_f32(p.dw_part + ((int64_t)g * s + j) * 256 * HS, 256, HS, HS, fin, wm * 64, wn * (HS / 2), lane, f);
+      store_tile_f32(p.dw_part + ((int64_t)g * s + j) * 256 * HS, 256, HS, HS, fin, wm * 64, wn * (HS / 2), lane,
+                     f);
     else
       store_tile_f32(p.dW + v0 * H + c0, V - v0, H, H - c0, fin, wm * 64, wn * (HS / 2), lane, f);
   }

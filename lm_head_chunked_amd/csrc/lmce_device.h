@@ -591,7 +591,6 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[MB][NB]) {
     for (int j = 0; j < NB; ++j) zero(acc[i][j]);
 }
 
-
 __device__ __forceinline__ float pick16(const f32x16& x, int reg) {
   float v = 0.f;
 #pragma unroll

@@ -194,6 +194,8 @@ hipError_t launch_bwd_group(int pass, const BwdArgs& a, int hs, int n_wgs, hipSt
 hipError_t launch_dh_finish(const BwdArgs& a, hipStream_t st);
 // Sums the dW pass's partial slices of its leftover blocks (no-op when none).
 hipError_t launch_dw_tail(const BwdArgs& a, int hs, hipStream_t st);
+// dW *= g/N after a dW pass with 128-wide slices (no-op for 256-wide ones,
+// which apply the factor when they store).
 hipError_t launch_dw_scale(const BwdArgs& a, int hs, hipStream_t st);
 
 }  // namespace lmce
