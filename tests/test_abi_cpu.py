@@ -195,3 +195,30 @@ def test_noalloc_forward_rejects_before_enqueuing(lib):
     assert f(FAKE, FAKE, FAKE, 512, 256, 4096, -100, 256, FAKE, None, None) == _lib.LMCE_ERR_NULL
     assert f(FAKE, FAKE, FAKE, (1 << 20) + 1, 256, 151936, -100, 256, FAKE, FAKE, None) == _lib.LMCE_ERR_SCRATCH
     assert f(FAKE, FAKE, FAKE, 1 << 21, 128, 1, -100, 256, FAKE, FAKE, None) == _lib.LMCE_ERR_SCRATCH
+
+
+def test_binding_refuses_host_tensors():
+    """The torch-level entry points take device tensors only: host tensors
+    raise before anything reaches the library (there is no CPU path)."""
+    import torch
+
+    import lm_head_chunked_amd as lm
+
+    h = torch.zeros(8, 128, dtype=torch.bfloat16)
+    W = torch.zeros(16, 128, dtype=torch.bfloat16)
+    y = torch.zeros(8, dtype=torch.int64)
+    for call in (lambda: lm.lmce_fwd(h, W, y), lambda: lm.lmce_fwd_train(h, W, y),
+                 lambda: lm.lmce_bwd(h, W, y, torch.zeros(8)), lambda: lm.lmce_chunked_fwd(h, W, y)):
+        try:
+            call()
+        except ValueError as e:
+            assert "device" in str(e)
+            continue
+        raise AssertionError("a host tensor was accepted")
+    x = torch.zeros(8, 128, dtype=torch.bfloat16)
+    try:
+        lm.lmce_mlp_fwd(x, W, W, W.t().contiguous(), 8)
+    except TypeError as e:
+        assert "device" in str(e)
+    else:
+        raise AssertionError("a host tensor was accepted by the MLP")

@@ -611,3 +611,38 @@ def test_row_shards_compose_to_the_whole(train):
     assert e_ref[0] <= LOSS_REL and e_ref[1] <= GRAD_REL and e_ref[2] <= GRAD_REL
     assert e_gpu[0] <= 1e-5 and e_gpu[1] <= 1e-5 and e_gpu[2] <= 1e-5
     assert np.all(dh_c[(y == -100).numpy()] == 0.0)
+
+
+def test_binding_rejects_bad_tensors_before_any_launch():
+    """The Python binding's checks: host tensors, wrong dtypes, mismatched or
+    non-contiguous shapes and a short workspace raise before the library is
+    called (the C ABI's own checks are covered on the CPU)."""
+    say("[case] binding argument checks")
+    dev = torch.device("cuda:0")
+    h, W, y = synth.random_case(64, 128, 300, seed=35)
+    hd, Wd, yd = h.to(dev), W.to(dev), y.to(dev)
+    bad = [
+        ((h, Wd, yd), ValueError),                                 # host tensor
+        ((hd.float(), Wd, yd), TypeError),                         # fp32 h
+        ((hd, Wd, yd.int()), TypeError),                           # int32 labels
+        ((hd, Wd[:, :64].contiguous(), yd), ValueError),           # H mismatch
+        ((hd, Wd, yd[:32].contiguous()), ValueError),              # L mismatch
+        ((hd.t().contiguous().t(), Wd, yd), ValueError),           # non-contiguous h
+        ((hd[None], Wd, yd), ValueError),                          # 3-D h
+    ]
+    for args, exc in bad:
+        with pytest.raises(exc):
+            lm.lmce_fwd(*args)
+    short = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError):
+        lm.lmce_fwd(hd, Wd, yd, workspace=short)
+    loss, lse = lm.lmce_fwd(hd, Wd, yd)
+    with pytest.raises(ValueError):
+        lm.lmce_bwd(hd, Wd, yd, lse.double())                     # lse must be fp32
+    x = torch.randn(32, 128, device=dev).to(torch.bfloat16)
+    Wg = torch.randn(64, 128, device=dev).to(torch.bfloat16)
+    with pytest.raises(TypeError):
+        lm.lmce_mlp_fwd(x.float(), Wg, Wg, Wg.t().contiguous(), 32)
+    with pytest.raises(ValueError):
+        lm.lmce_mlp_fwd(x, Wg, Wg, Wg.contiguous(), 32)           # Wd must be [H, I]
+    torch.cuda.synchronize()
