@@ -41,6 +41,12 @@
  *     lmce_read_status, which is documented as synchronising).
  *   - The caller supplies a workspace of at least lmce_workspace_size()
  *     bytes.  Calls that share a workspace must be ordered on one stream.
+ *   - The group-scheduled passes (lmce_fwd_train, lmce_bwd_train, lmce_bwd,
+ *     lmce_bwd_dh, lmce_bwd_dW) launch one cooperative grid sized to the
+ *     whole device; running two of them at once on one device (other
+ *     streams or processes) is not supported.  Every group wait is bounded,
+ *     so members that cannot all be resident end the call with LMCE_ERR_HIP
+ *     from lmce_read_status rather than a hang.
  *   - Return value: LMCE_OK (0) or a negative lmce_status.  Argument errors
  *     are detected before anything is enqueued.
  *   - Limits: 1 <= L <= 2^21, 1 <= V <= 2^21, 128 <= H <= 16384 with
