@@ -53,7 +53,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["mlp_forward", "mlp_backward", "mlp_fwd_bwd", "mlp_rows_forward", "mlp_rows_dx"]
+__all__ = ["mlp_forward", "mlp_backward", "mlp_fwd_bwd", "mlp_rows_forward", "mlp_rows_dx", "mlp_cols_grads"]
 
 
 def _widen(a, name):
@@ -143,3 +143,36 @@ def mlp_rows_forward(x_rows, Wg, Wu, Wd):
 def mlp_rows_dx(x_rows, Wg, Wu, Wd, dy_rows):
     """dx for a subset of rows: each row of dx depends on its own x and dy rows only."""
     return mlp_backward(x_rows, Wg, Wu, Wd, dy_rows, block_rows=max(1, np.asarray(x_rows).shape[0]))[0]
+
+
+def mlp_cols_grads(x, Wg, Wu, Wd, dy, cols, block_rows=8192):
+    """The weight gradients of chosen intermediate units i in cols, over all rows:
+    (dWg[cols] [c, H], dWu[cols] [c, H], dWd[:, cols] [H, c]) in float64.
+
+    Unit i's gradients need only its own column of g, u and dp (g_i = x Wg_i,
+    u_i = x Wu_i, dp_i = dy Wd[:, i]), so a few units can be checked where the
+    whole backward would be too slow.
+    """
+    x64, Wg64, Wu64, Wd64 = (_widen(t, n) for t, n in ((x, "x"), (Wg, "Wg"), (Wu, "Wu"), (Wd, "Wd")))
+    L, H, I = _shapes(x64, Wg64, Wu64, Wd64)
+    cols = np.asarray(cols).astype(np.int64, copy=False)
+    if np.any((cols < 0) | (cols >= I)):
+        raise ValueError("cols must index the intermediate units")
+    dy64 = _widen(dy, "dy")
+    if dy64.shape != (L, H):
+        raise ValueError("dy must have the shape of y")
+    Wgc, Wuc, Wdc = Wg64[cols], Wu64[cols], Wd64[:, cols]
+    dWgc = np.zeros((cols.shape[0], H), dtype=np.float64)
+    dWuc = np.zeros((cols.shape[0], H), dtype=np.float64)
+    dWdc = np.zeros((H, cols.shape[0]), dtype=np.float64)
+    for r0 in range(0, L, block_rows):
+        r1 = min(L, r0 + block_rows)
+        xb, dyb = x64[r0:r1], dy64[r0:r1]
+        gc, uc, s, a = _block(xb, Wgc, Wuc)
+        dWdc += dyb.T @ (a * uc)
+        dpc = dyb @ Wdc
+        duc = dpc * a
+        dgc = dpc * uc * s * (1.0 + gc * (1.0 - s))
+        dWgc += dgc.T @ xb
+        dWuc += duc.T @ xb
+    return dWgc, dWuc, dWdc

@@ -174,6 +174,19 @@ def pin_mlp_row_helpers(orc):
     assert np.max(np.abs(orc.mlp_rows_dx(x[rows], Wg, Wu, Wd, dy[rows]) - o["dx"][rows])) <= 1e-13
 
 
+def pin_mlp_col_helper(orc):
+    """The chosen-unit weight-gradient helper agrees with the full arrays, for
+    the first, last and inner units and row blocks that split the rows
+    unevenly."""
+    x, Wg, Wu, Wd, dy = _case(29, 8, 16, seed=8)
+    o = orc.mlp_fwd_bwd(x, Wg, Wu, Wd, dy)
+    cols = np.array([0, 5, 6, 15])
+    for b in (4, 8192):
+        dWg, dWu, dWd = orc.mlp_cols_grads(x, Wg, Wu, Wd, dy, cols, block_rows=b)
+        for got, ref in ((dWg, o["dWg"][cols]), (dWu, o["dWu"][cols]), (dWd, o["dWd"][:, cols])):
+            assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref))), b
+
+
 ALL_MLP_PINS = [
     pin_mlp_zero_weights,
     pin_mlp_silu_values,
@@ -182,4 +195,5 @@ ALL_MLP_PINS = [
     pin_mlp_finite_differences,
     pin_mlp_row_blocks,
     pin_mlp_row_helpers,
+    pin_mlp_col_helper,
 ]

@@ -103,7 +103,9 @@ def test_mlp_qwen3_4b_shape_full_oracle():
 
 def test_mlp_qwen3_4b_full_workload_sampled():
     """262,144 rows at chunk 16384: y and dx of 512 sampled rows against the
-    oracle's row helpers; the weight gradients against a run at chunk 8192."""
+    oracle's row helpers; the weight gradients of 8 sampled units over all
+    rows against the oracle's unit helper, and in full against a run at chunk
+    8192."""
     wl = synth.MLP_WORKLOADS["qwen3_4b_mlp_256k"]
     say(f"[case] Qwen3-4B MLP full workload L={wl.L} H={wl.H} I={wl.I}")
     dev = torch.device("cuda:0")
@@ -125,3 +127,10 @@ def test_mlp_qwen3_4b_full_workload_sampled():
     e_y, e_dx = rel_fro(np32(a["y"][rd]), y_ref), rel_fro(np32(a["dx"][rd]), dx_ref)
     say(f"[mlp full] sampled rows: y {e_y:.2e} dx {e_dx:.2e}")
     assert e_y <= REL and e_dx <= REL
+    cols = torch.unique(torch.cat([torch.tensor([0, wl.I - 1]), torch.randperm(wl.I, generator=g)[:6]]))
+    cd = cols.to(dev)
+    dWg_ref, dWu_ref, dWd_ref = oracle.mlp_cols_grads(np32(x), *W_np, np32(dy), cols.numpy())
+    errs = (rel_fro(np32(a["dWg"][cd]), dWg_ref), rel_fro(np32(a["dWu"][cd]), dWu_ref),
+            rel_fro(np32(a["dWd"][:, cd]), dWd_ref))
+    say(f"[mlp full] {len(cols)} sampled units over all rows: dWg {errs[0]:.2e} dWu {errs[1]:.2e} dWd {errs[2]:.2e}")
+    assert max(errs) <= REL

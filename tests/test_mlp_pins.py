@@ -21,6 +21,9 @@ MUTATIONS = {
     "dWd_overwritten_per_block": ("dWd += dyb.T @ (a * u)", "dWd = dyb.T @ (a * u)"),
     "dWg_from_up": ("dWg += dg.T @ xb", "dWg += du.T @ xb"),
     "dp_transposed_weight": ("dp = dyb @ Wd64\n", "dp = dyb @ Wd64[:, ::-1]\n"),
+    "cols_dsilu_missing_term": ("dgc = dpc * uc * s * (1.0 + gc * (1.0 - s))", "dgc = dpc * uc * s"),
+    "cols_du_uses_gate": ("duc = dpc * a\n", "duc = dpc * gc\n"),
+    "cols_dWd_first_block_only": ("dWdc += dyb.T @ (a * uc)", "dWdc += dyb.T @ (a * uc) if r0 == 0 else 0.0"),
 }
 
 
